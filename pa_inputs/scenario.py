@@ -1,0 +1,118 @@
+"""Each workload as an op list: the allocator and pool calls to make, in order.
+
+An op list is data.  Each side (the oracle's tests, the library's callers)
+runs it with its own allocator, its own pool writes and its own attention, so
+the two share the sequence of requests and the random values but no code that
+computes anything.
+
+Ops in ``setup``:
+  ("add", seq)                        open an empty sequence
+  ("append", seq, n)                  reserve n slots for seq and write the
+                                      sequence's history K/V (``history``)
+  ("fork", parent, child)             child shares all of parent's blocks
+  ("churn",)                          run ``gen.churn`` against the allocator
+
+Each ``Step`` then: one batched append (``appends`` in order, K/V rows
+``k_new``/``v_new`` in the same order, copy-on-write pairs first), then decode
+attention for ``decode_seqs`` with queries ``q`` and, when present, one causal
+prefill chunk.
+"""
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Tuple
+
+import numpy as np
+
+from . import gen
+from .configs import config as make_config
+
+
+@dataclass
+class Prefill:
+    seq: int
+    ctx_before: int
+    T: int
+    q: np.ndarray  # float32 [T][H_q][d]
+
+
+@dataclass
+class Step:
+    appends: List[Tuple[int, int]]
+    k_new: np.ndarray  # float32 [T][H_kv][d]
+    v_new: np.ndarray
+    decode_seqs: List[int]
+    q: np.ndarray  # float32 [len(decode_seqs)][H_q][d]
+    prefill: Optional[Prefill] = None
+
+
+@dataclass
+class Scenario:
+    cfg: dict
+    seed: int
+    setup: list = field(default_factory=list)
+    steps: List[Step] = field(default_factory=list)
+    ctx: Optional[np.ndarray] = None  # per decode sequence, before the first step
+
+    def history(self, seq, n):
+        """History K/V of ``seq``'s first n tokens (float32 [n][H_kv][d] each)."""
+        return gen.history_kv(self.cfg, self.seed, seq, n)
+
+
+def _decode_batch(cfg, seed, seqs, step_index):
+    T = len(seqs)
+    k, v = gen.new_kv(cfg, seed, step_index, T)
+    q = gen.queries(cfg, seed, step_index, T)
+    return Step(appends=[(s, 1) for s in seqs], k_new=k, v_new=v, decode_seqs=list(seqs), q=q)
+
+
+def build_scenario(cid, seed=0, **overrides):
+    cfg = make_config(cid, **overrides)
+    scn = Scenario(cfg=cfg, seed=seed)
+    kind = cfg["kind"]
+    if kind == "decode":
+        ctx = gen.lengths(cfg, seed)
+        scn.ctx = ctx
+        if cfg.get("churn_rounds"):
+            scn.setup.append(("churn",))
+        for s, n in enumerate(ctx):
+            scn.setup.append(("add", s))
+            scn.setup.append(("append", s, int(n)))
+        scn.steps.append(_decode_batch(cfg, seed, list(range(cfg["B"])), 0))
+    elif kind == "fork":
+        P, S = cfg["prompts"], cfg["samples"]
+        for p in range(P):
+            root = p * S
+            scn.setup.append(("add", root))
+            scn.setup.append(("append", root, cfg["prefix"]))
+            for s in range(1, S):
+                scn.setup.append(("fork", root, root + s))
+        seqs = list(range(P * S))
+        scn.ctx = np.full(P * S, cfg["prefix"], dtype=np.int64)
+        # tail: every sample writes its own 32 tokens after the shared prefix
+        T = len(seqs) * cfg["tail"]
+        k, v = gen.new_kv(cfg, seed, 0, T)
+        scn.steps.append(Step(appends=[(s, cfg["tail"]) for s in seqs], k_new=k, v_new=v,
+                              decode_seqs=[], q=np.zeros((0, cfg["H_q"], cfg["d"]), np.float32)))
+        for i in range(cfg["steps"]):
+            scn.steps.append(_decode_batch(cfg, seed, seqs, 1 + i))
+    elif kind == "mixed":
+        ctx = gen.lengths(cfg, seed)
+        scn.ctx = ctx
+        B = cfg["B"]
+        for s, n in enumerate(ctx):
+            scn.setup.append(("add", s))
+            scn.setup.append(("append", s, int(n)))
+        pseq = B
+        scn.setup.append(("add", pseq))
+        scn.setup.append(("append", pseq, cfg["ctx_before"]))
+        st = _decode_batch(cfg, seed, list(range(B)), 0)
+        kc, vc = gen.chunk_kv(cfg, seed, cfg["chunk"])
+        st.appends.append((pseq, cfg["chunk"]))
+        st.k_new = np.concatenate([st.k_new, kc])
+        st.v_new = np.concatenate([st.v_new, vc])
+        st.prefill = Prefill(seq=pseq, ctx_before=cfg["ctx_before"], T=cfg["chunk"],
+                             q=gen.chunk_queries(cfg, seed, cfg["chunk"]))
+        scn.steps.append(st)
+    else:
+        raise ValueError(kind)
+    return scn
