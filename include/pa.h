@@ -1,0 +1,187 @@
+/*
+ * pa.h -- C ABI of a paged KV cache and PagedAttention hot path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, site, section heading):
+ *   [youngju] "vLLM 내부 구조 (2) — PagedAttention은 KV 캐시를 왜 페이지로 쪼갰는가",
+ *             youngju.dev
+ *   [icarus]  "PagedAttention", icarus.shaojiemike.top
+ *   [ttlab]   "llm-kv-cache-02-serving-engine-kv", ttlab.hopto.org
+ *
+ * Conventions for every call below
+ *   - Device pointers point at memory the caller allocated (hipMalloc or a
+ *     torch tensor).  The library never allocates, frees or synchronises;
+ *     each call only enqueues kernels on ``stream`` and returns.  The caller
+ *     orders calls on one stream: copy-on-write copies, then appends, then
+ *     attention.
+ *   - ``pa_kv_pool`` is a host struct, read during the call only.
+ *   - Return value: PA_OK (0) or a negative PA_E* code.  On an error nothing
+ *     has been enqueued.  ``pa_status_string`` gives a message; for PA_EHIP
+ *     it also carries the HIP error text of the failed launch.
+ *   - Device-side contents (block ids, slots, copy pairs) are trusted: the
+ *     kernels do not range-check them.  Host-side sizes are checked.
+ *   - Element types: PA_F32, PA_BF16, PA_F16.  Queries, new K/V and outputs
+ *     use the pool's element type.  Arithmetic is fp32; outputs are rounded
+ *     to nearest-even.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_EINVAL = -1,  /* null pointer, bad size, head counts that do not divide, layer out of range */
+  PA_ENOTSUP = -2, /* a (dtype, head_dim, block_size, query-group) combination that is not compiled */
+  PA_ENOMEM = -3,  /* the block manager has too few free blocks (state unchanged) */
+  PA_EHIP = -4,    /* a kernel launch failed */
+  PA_ENOENT = -5,  /* the block manager has no such sequence (or it already exists) */
+  PA_ESPACE = -6   /* an output buffer or workspace is too small */
+};
+
+/*
+ * The physical block pool.  KV is cut into fixed-size blocks of
+ * ``block_size`` token slots held in one shared pool ([youngju] "블록 테이블:
+ * 논리적으로 연속, 물리적으로 흩어짐"; [ttlab] "블록과 블록 표"); the kernel
+ * reads K/V by layer, KV head, token and head dimension ([icarus] "类比的边界").
+ *
+ * k, v: device, each [num_layers][num_kv_heads][num_blocks][block_size][head_dim]
+ * row-major, element type ``dtype``.  One block of one head is a contiguous
+ * block_size * head_dim run (4 KiB for 16 x 128 bf16).  Slot s of a layer and
+ * head is token s % block_size of block s / block_size.
+ */
+typedef struct pa_kv_pool {
+  void* k;
+  void* v;
+  int32_t num_layers;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t block_size; /* 8, 16 or 32 */
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t dtype;      /* pa_dtype */
+} pa_kv_pool;
+
+/*
+ * Append: write each new token's K/V into its slot of the current block
+ * ([icarus] "Block Table 如何工作"; [ttlab] "블록과 블록 표").
+ *   k_new, v_new: device [T][num_kv_heads][head_dim], pool dtype.
+ *   slot_mapping: device int32 [T]; a negative slot skips that row.  Slots
+ *                 must be distinct and < num_blocks * block_size.
+ *   T >= 0 (T == 0 enqueues nothing).
+ * A bit copy: pool bytes equal the input bytes.
+ */
+int pa_cache_append(const pa_kv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                    const int32_t* slot_mapping, int32_t T, hipStream_t stream);
+
+/*
+ * Copy-on-write block copies: a block shared by several sequences is copied
+ * only when one of them must write into it ([icarus] "支持块级共享"; [ttlab]
+ * "블록을 함께 쓰기").
+ *   pairs: device int32 [n][2] = (src, dst) physical block ids.  For each
+ *          pair, the whole block -- every layer, every KV head, K and V -- is
+ *          copied bit for bit.  No dst may appear as another pair's src or dst.
+ *   n >= 0.
+ */
+int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t n, hipStream_t stream);
+
+/*
+ * Workspace bytes ``pa_decode`` needs for a batch (0 when it will not split a
+ * sequence over several workgroups).  Depends on host-side sizes only.
+ */
+size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t B, int32_t H_q, int32_t max_ctx);
+
+/*
+ * Decode attention: each sequence's newest query reads all of its visible
+ * K/V, found through its block table, and computes softmax(scale * q K^T) V
+ * ([icarus] "Block Table 如何工作", "KV Cache 为什么难管理" and
+ * "不会降低单请求的理论读取量"; [ttlab] "블록과 블록 표").
+ *   out: device [B][H_q][head_dim], pool dtype (written for every sequence;
+ *        a sequence with context_lens == 0 gets zeros).
+ *   q:   device [B][H_q][head_dim], pool dtype.
+ *   H_q: a multiple of num_kv_heads; query head h reads KV head
+ *        h / (H_q / num_kv_heads).
+ *   block_tables: device int32 [B][max_blocks]; entry j of row i is the
+ *        physical block holding tokens j*block_size .. of sequence i.
+ *   context_lens: device int32 [B], visible tokens per sequence (the token
+ *        just appended included); each <= max_ctx and
+ *        <= max_blocks * block_size.
+ *   max_ctx: host upper bound of context_lens, used to size the grid.
+ *   scale: multiplies q.k before the softmax.
+ *   workspace: device, at least pa_decode_workspace_size(...) bytes
+ *        (may be NULL when that is 0).  Contents need no initialisation.
+ */
+int pa_decode(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B, int32_t H_q,
+              const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t max_ctx,
+              float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Causal prefill chunk over paged K/V: a long prompt is processed in chunks
+ * ([ttlab] "새 문제: 긴 프리필이 디코드를 멈춘다"); chunk row t sits at position
+ * ctx_before + t and attends to positions 0 .. ctx_before + t of its own
+ * sequence ([icarus] "KV Cache 为什么难管理").  The chunk's own K/V must
+ * already be appended.  bf16 and f16 pools only (matrix cores).
+ *   out, q: device [T][H_q][head_dim], pool dtype.
+ *   block_table: device int32 [nb], nb >= ceil((ctx_before + T) / block_size).
+ */
+int pa_prefill_chunk(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t T, int32_t H_q,
+                     const int32_t* block_table, int32_t nb, int32_t ctx_before, float scale,
+                     hipStream_t stream);
+
+/* Message for a status code (thread-local copy of the last error detail). */
+const char* pa_status_string(int status);
+
+/*
+ * Host block manager: the bookkeeping that produces block tables, slots and
+ * copy-on-write pairs ([icarus] "Block Table 如何工作" and "支持块级共享";
+ * [ttlab] "블록과 블록 표" and "블록을 함께 쓰기").
+ *
+ *   - Free pool: a FIFO queue initialised with ``free_order`` (a permutation
+ *     of 0 .. num_blocks-1); allocation takes the front.
+ *   - append_slots(seq, n): for each new position p, block j = p / block_size;
+ *     if j is one past the table's end, take a free block; else if that
+ *     block's refcount is above 1, copy-on-write: take a free block, emit
+ *     (old, new), drop old's count by one.  slot = table[j]*block_size +
+ *     p % block_size.  At most one copy-on-write pair per call.
+ *   - fork(parent, child): child's table = parent's; every block's count +1.
+ *   - free_seq(seq): walking the table from its last block to its first,
+ *     drop each count; blocks reaching 0 go to the back of the free queue.
+ *   - Out of blocks: PA_ENOMEM, nothing changed.
+ * The handle is not thread-safe.  Sequence ids are any int32 values.
+ */
+typedef struct pa_bm pa_bm;
+
+int pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pa_bm** out);
+void pa_bm_destroy(pa_bm* bm);
+int pa_bm_add_seq(pa_bm* bm, int32_t seq);
+int pa_bm_fork(pa_bm* bm, int32_t parent, int32_t child);
+/* slots_out: host int32 [n]; cow_pairs_out: host int32 [2] (may be NULL only if no pair results). */
+int pa_bm_append_slots(pa_bm* bm, int32_t seq, int32_t n, int32_t* slots_out, int32_t* cow_pairs_out,
+                       int32_t* n_cow_out);
+/* Batched form: for i in order, append ns[i] slots to seqs[i].  slots_out: host [sum ns];
+ * cow_pairs_out: host int32 [2*count].  All-or-nothing: on PA_ENOMEM no sequence changes. */
+int pa_bm_append_slots_batch(pa_bm* bm, const int32_t* seqs, const int32_t* ns, int32_t count, int32_t* slots_out,
+                             int32_t* cow_pairs_out, int32_t* n_cow_out);
+int pa_bm_free_seq(pa_bm* bm, int32_t seq);
+/* Copies up to cap entries of seq's table to out; *n_out = full table length. */
+int pa_bm_block_table(pa_bm* bm, int32_t seq, int32_t* out, int32_t cap, int32_t* n_out);
+/* Writes a [count][max_blocks] table (rows padded with pad) for seqs[0..count). */
+int pa_bm_block_tables(pa_bm* bm, const int32_t* seqs, int32_t count, int32_t* out, int32_t max_blocks,
+                       int32_t pad);
+int pa_bm_seq_len(pa_bm* bm, int32_t seq);  /* >= 0, or PA_ENOENT */
+int pa_bm_refcount(pa_bm* bm, int32_t block); /* >= 0, or PA_EINVAL */
+int pa_bm_num_free(pa_bm* bm);
+int pa_bm_free_list(pa_bm* bm, int32_t* out, int32_t cap); /* returns the count; copies up to cap */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,19 @@
+"""Paged KV cache and PagedAttention hot path for AMD MI355X (gfx950).
+
+The work is done by ``libpa.so`` (hand-written HIP kernels behind the C ABI
+of ``include/pa.h``); this package marshals torch tensors into those calls
+and wraps the host block manager.
+"""
+
+from ._lib import PAError, lib, status_string  # noqa: F401
+from .api import (  # noqa: F401
+    BlockManager,
+    KVPool,
+    OutOfBlocks,
+    decode_workspace,
+    pa_cache_append,
+    pa_copy_blocks,
+    pa_decode,
+    pa_decode_workspace_size,
+    pa_prefill_chunk,
+)

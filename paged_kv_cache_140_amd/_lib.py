@@ -1,0 +1,90 @@
+"""ctypes loader for ``libpa.so`` and the C structs / signatures of ``include/pa.h``.
+
+The library is built in-tree (``python -m paged_kv_cache_140_amd.build``).
+If it is missing, every entry point raises: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_F32, PA_BF16, PA_F16 = 0, 1, 2
+PA_OK, PA_EINVAL, PA_ENOTSUP, PA_ENOMEM, PA_EHIP, PA_ENOENT, PA_ESPACE = 0, -1, -2, -3, -4, -5, -6
+
+# Every symbol pa.h declares, with (restype, argtypes).
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class KVPoolStruct(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("num_layers", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_PPOOL = ctypes.POINTER(KVPoolStruct)
+
+SIGNATURES = {
+    "pa_cache_append": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _p, _i32, _p]),
+    "pa_copy_blocks": (ctypes.c_int, [_PPOOL, _p, _i32, _p]),
+    "pa_decode_workspace_size": (ctypes.c_size_t, [_PPOOL, _i32, _i32, _i32]),
+    "pa_decode": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _p, _i32, ctypes.c_float, _p,
+                                 ctypes.c_size_t, _p]),
+    "pa_prefill_chunk": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _i32, ctypes.c_float, _p]),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_bm_create": (ctypes.c_int, [_i32, _i32, _pi32, ctypes.POINTER(_p)]),
+    "pa_bm_destroy": (None, [_p]),
+    "pa_bm_add_seq": (ctypes.c_int, [_p, _i32]),
+    "pa_bm_fork": (ctypes.c_int, [_p, _i32, _i32]),
+    "pa_bm_append_slots": (ctypes.c_int, [_p, _i32, _i32, _pi32, _pi32, _pi32]),
+    "pa_bm_append_slots_batch": (ctypes.c_int, [_p, _pi32, _pi32, _i32, _pi32, _pi32, _pi32]),
+    "pa_bm_free_seq": (ctypes.c_int, [_p, _i32]),
+    "pa_bm_block_table": (ctypes.c_int, [_p, _i32, _pi32, _i32, _pi32]),
+    "pa_bm_block_tables": (ctypes.c_int, [_p, _pi32, _i32, _pi32, _i32, _i32]),
+    "pa_bm_seq_len": (ctypes.c_int, [_p, _i32]),
+    "pa_bm_refcount": (ctypes.c_int, [_p, _i32]),
+    "pa_bm_num_free": (ctypes.c_int, [_p]),
+    "pa_bm_free_list": (ctypes.c_int, [_p, _pi32, _i32]),
+}
+
+_lib = None
+
+
+class PAError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def lib():
+    """Load ``libpa.so`` once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_140_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status):
+    return lib().pa_status_string(int(status)).decode()
+
+
+def check(status, where):
+    if status != PA_OK:
+        raise PAError(status, where)
+    return status

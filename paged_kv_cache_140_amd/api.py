@@ -1,0 +1,230 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch
+tensors for device buffers.  Every step of the hot path runs in the HIP
+kernels of ``libpa.so``; nothing here computes on the data.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import KVPoolStruct, PAError, check, lib
+
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+PA_DTYPE = {"f32": _lib.PA_F32, "bf16": _lib.PA_BF16, "f16": _lib.PA_F16}
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+class KVPool:
+    """The physical block pool: K and V, each [layers][kv_heads][blocks][block_size][head_dim].
+
+    Device memory comes from torch; the library only reads and writes it.
+    """
+
+    def __init__(self, num_layers, num_kv_heads, num_blocks, block_size, head_dim, dtype, device="cuda",
+                 k=None, v=None):
+        self.num_layers, self.num_kv_heads, self.num_blocks = num_layers, num_kv_heads, num_blocks
+        self.block_size, self.head_dim, self.dtype = block_size, head_dim, dtype
+        shape = (num_layers, num_kv_heads, num_blocks, block_size, head_dim)
+        self.k = k if k is not None else torch.empty(shape, dtype=TORCH_DTYPE[dtype], device=device)
+        self.v = v if v is not None else torch.empty(shape, dtype=TORCH_DTYPE[dtype], device=device)
+        _need(self.k, "pool.k", TORCH_DTYPE[dtype], shape)
+        _need(self.v, "pool.v", TORCH_DTYPE[dtype], shape)
+
+    @property
+    def torch_dtype(self):
+        return TORCH_DTYPE[self.dtype]
+
+    def struct(self):
+        return KVPoolStruct(self.k.data_ptr(), self.v.data_ptr(), self.num_layers, self.num_kv_heads,
+                            self.num_blocks, self.block_size, self.head_dim, PA_DTYPE[self.dtype])
+
+    def nbytes(self):
+        return 2 * self.k.numel() * self.k.element_size()
+
+
+def pa_cache_append(pool, layer, k_new, v_new, slot_mapping, stream=None):
+    T = int(k_new.shape[0])
+    row = (T, pool.num_kv_heads, pool.head_dim)
+    _need(k_new, "k_new", pool.torch_dtype, row)
+    _need(v_new, "v_new", pool.torch_dtype, row)
+    _need(slot_mapping, "slot_mapping", torch.int32, (T,))
+    s = pool.struct()
+    check(lib().pa_cache_append(ctypes.byref(s), layer, _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T,
+                                _stream(stream)), "pa_cache_append")
+
+
+def pa_copy_blocks(pool, pairs, stream=None):
+    n = int(pairs.shape[0])
+    _need(pairs, "pairs", torch.int32, (n, 2))
+    s = pool.struct()
+    check(lib().pa_copy_blocks(ctypes.byref(s), _ptr(pairs), n, _stream(stream)), "pa_copy_blocks")
+
+
+def pa_decode_workspace_size(pool, B, H_q, max_ctx):
+    s = pool.struct()
+    return int(lib().pa_decode_workspace_size(ctypes.byref(s), B, H_q, max_ctx))
+
+
+def pa_decode(pool, layer, out, q, block_tables, context_lens, max_ctx, scale, workspace=None, stream=None):
+    B, H_q, d = (int(x) for x in q.shape)
+    _need(q, "q", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(out, "out", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B][max_blocks]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    s = pool.struct()
+    check(lib().pa_decode(ctypes.byref(s), layer, _ptr(out), _ptr(q), B, H_q, _ptr(block_tables),
+                          int(block_tables.shape[1]), _ptr(context_lens), int(max_ctx), float(scale),
+                          _ptr(workspace), ws_bytes, _stream(stream)), "pa_decode")
+
+
+def pa_prefill_chunk(pool, layer, out, q, block_table, ctx_before, scale, stream=None):
+    T, H_q, d = (int(x) for x in q.shape)
+    _need(q, "q", pool.torch_dtype, (T, H_q, pool.head_dim))
+    _need(out, "out", pool.torch_dtype, (T, H_q, pool.head_dim))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 1:
+        raise ValueError("block_table must be 1-D")
+    s = pool.struct()
+    check(lib().pa_prefill_chunk(ctypes.byref(s), layer, _ptr(out), _ptr(q), T, H_q, _ptr(block_table),
+                                 int(block_table.shape[0]), int(ctx_before), float(scale), _stream(stream)),
+          "pa_prefill_chunk")
+
+
+def decode_workspace(pool, B, H_q, max_ctx, device="cuda"):
+    """A workspace tensor of the size pa_decode needs (None if it needs none)."""
+    n = pa_decode_workspace_size(pool, B, H_q, max_ctx)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------- allocator
+
+class OutOfBlocks(PAError):
+    pass
+
+
+def _arr(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class BlockManager:
+    """Host block manager (``pa_bm_*``): free queue, tables, refcounts, CoW."""
+
+    def __init__(self, num_blocks, block_size, free_order):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        order, p = _arr(free_order)
+        if order.shape != (self.num_blocks,):
+            raise ValueError("free_order must have num_blocks entries")
+        h = ctypes.c_void_p()
+        check(lib().pa_bm_create(self.num_blocks, self.block_size, p, ctypes.byref(h)), "pa_bm_create")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib._lib is not None:
+            _lib._lib.pa_bm_destroy(h)
+            self._h = None
+
+    def _check(self, st, where):
+        if st == _lib.PA_ENOMEM:
+            raise OutOfBlocks(st, where)
+        return check(st, where)
+
+    def add_seq(self, seq):
+        self._check(lib().pa_bm_add_seq(self._h, int(seq)), "pa_bm_add_seq")
+
+    def fork(self, parent, child):
+        self._check(lib().pa_bm_fork(self._h, int(parent), int(child)), "pa_bm_fork")
+
+    def free_seq(self, seq):
+        self._check(lib().pa_bm_free_seq(self._h, int(seq)), "pa_bm_free_seq")
+
+    def append_slots(self, seq, n):
+        """-> (slots int32 [n], list of (src, dst) pairs)."""
+        slots, ps = _arr(np.zeros(max(int(n), 1)))
+        pair, pp = _arr(np.zeros(2))
+        npair = ctypes.c_int32(0)
+        self._check(lib().pa_bm_append_slots(self._h, int(seq), int(n), ps, pp, ctypes.byref(npair)),
+                    "pa_bm_append_slots")
+        return slots[:int(n)].copy(), ([(int(pair[0]), int(pair[1]))] if npair.value else [])
+
+    def append_slots_batch(self, seqs, ns):
+        """All-or-nothing batch -> (slots int32 [sum ns], pairs int32 [k][2])."""
+        seqs_a, sp = _arr(seqs)
+        ns_a, np_ = _arr(ns)
+        total = int(ns_a.sum())
+        slots, slp = _arr(np.zeros(max(total, 1)))
+        pairs, pp = _arr(np.zeros(2 * max(len(seqs_a), 1)))
+        npair = ctypes.c_int32(0)
+        self._check(lib().pa_bm_append_slots_batch(self._h, sp, np_, len(seqs_a), slp, pp, ctypes.byref(npair)),
+                    "pa_bm_append_slots_batch")
+        return slots[:total].copy(), pairs[:2 * npair.value].reshape(-1, 2).copy()
+
+    def block_table(self, seq):
+        n = ctypes.c_int32(0)
+        self._check(lib().pa_bm_block_table(self._h, int(seq), None, 0, ctypes.byref(n)), "pa_bm_block_table")
+        out, p = _arr(np.zeros(max(n.value, 1)))
+        self._check(lib().pa_bm_block_table(self._h, int(seq), p, n.value, ctypes.byref(n)), "pa_bm_block_table")
+        return [int(x) for x in out[:n.value]]
+
+    def block_tables(self, seqs, max_blocks, pad=0):
+        seqs_a, sp = _arr(seqs)
+        out, p = _arr(np.zeros((len(seqs_a), max_blocks)))
+        self._check(lib().pa_bm_block_tables(self._h, sp, len(seqs_a), p, int(max_blocks), int(pad)),
+                    "pa_bm_block_tables")
+        return out
+
+    def seq_len(self, seq):
+        st = lib().pa_bm_seq_len(self._h, int(seq))
+        if st < 0:
+            self._check(st, "pa_bm_seq_len")
+        return st
+
+    def refcount(self, block):
+        st = lib().pa_bm_refcount(self._h, int(block))
+        if st < 0:
+            self._check(st, "pa_bm_refcount")
+        return st
+
+    def num_free(self):
+        return lib().pa_bm_num_free(self._h)
+
+    def free_list(self):
+        n = lib().pa_bm_free_list(self._h, None, 0)
+        out, p = _arr(np.zeros(max(n, 1)))
+        lib().pa_bm_free_list(self._h, p, n)
+        return [int(x) for x in out[:n]]
