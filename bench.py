@@ -1,0 +1,307 @@
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: the Qwen3-1.7B-shaped decode layer -- B=32 sequences, 16 query /
+8 KV heads, head_dim 128, 16-token blocks, contexts uniform in [512, 640],
+a 1,378-block (22,048-token) pool per layer, bf16.  One step = the step's
+append (one new token per sequence) + paged decode attention, on resident
+device inputs.  The pool holds 28 layers sharing one block table and each
+step works on the next layer, as a model's layer loop does, so every step
+reads its K/V from HBM rather than from the 256 MB Infinity Cache.
+
+Prints one JSON line.  ``value`` is decode KV-read GB/s over the whole step
+(append + decode); ``roofline`` rates the decode kernel alone; the second
+half of the metric, attention tokens/s at B=64, is measured on the 13B-shaped
+B=64 workload and reported as ``attention_tok_s_b64``.  ``rows`` gives the
+other hot-path rows on the workloads that exercise them.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=28, help="layers the step rotates over (cache-cold reads)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample length")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the other workloads' rows")
+    ap.add_argument("--copy-calibration-mib", type=int, default=512,
+                    help="size of a plain device copy run once before timing (counter calibration)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ bytes/flops
+
+def decode_bytes(lens, H_kv, H_q, d, bs, s):
+    """Algorithmic bytes of one decode: every visible K and V once per KV head,
+    q and out, and the block-table entries read."""
+    lens = [int(x) for x in lens]
+    kv = sum(lens) * H_kv * d * 2 * s
+    qo = 2 * len(lens) * H_q * d * s
+    tables = 4 * sum(-(-n // bs) for n in lens)
+    return kv + qo + tables
+
+
+def append_bytes(T, H_kv, d, s):
+    return 2 * (2 * T * H_kv * d * s) + 4 * T
+
+
+def prefill_flops(T, H_q, d, ctx_before):
+    return 4 * H_q * d * (T * ctx_before + T * (T + 1) // 2)
+
+
+# ------------------------------------------------------------------ timing
+
+def time_loop(torch, fn, iters, warmup):
+    """Average ms per call of fn(i) over ``iters`` consecutive calls.
+
+    ``warmup`` eager calls first; then the ``iters`` calls are captured in one
+    HIP graph (the library enqueues plain kernel launches, no memsets), the
+    graph is replayed once untimed, and one more replay is timed with events
+    on the current stream.  A graph keeps the host's per-call marshalling
+    (tens of microseconds of Python) out of kernels that take ~10 us.
+    """
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(warmup + i)
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / iters
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the hot path is measured on one GPU's share; "
+                                   "run with --gpus 1"}), flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        return 2
+    import paged_kv_cache_140_amd as pa  # raises if libpa.so is missing
+    from paged_kv_cache_140_amd.runner import GpuRun
+    from pa_inputs import build_scenario
+
+    pa.lib()
+    dev = "cuda"
+    t_start = time.time()
+
+    # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE under rocprofv3
+    # calibrate the counters of the kernels below.
+    nbytes = args.copy_calibration_mib << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).random_()
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+    # ---------------------------------------------------------- headline: config 2
+    scn = build_scenario(2, 0)
+    cfg = scn.cfg
+    L = args.layers
+    gpu = GpuRun(scn, device=dev, num_layers=L, fill="randn")
+    gpu.run_setup()
+    step = scn.steps[0]
+    si = gpu.prepare(step)
+    lens = si.lens.cpu().numpy()
+    s = 2
+    dbytes = decode_bytes(lens, cfg["H_kv"], cfg["H_q"], cfg["d"], cfg["bs"], s)
+    abytes = append_bytes(len(step.appends), cfg["H_kv"], cfg["d"], s)
+
+    def full_step(i):
+        gpu.layer = i % L
+        gpu.launch(si)
+
+    def decode_only(i):
+        gpu.layer = i % L
+        gpu.launch(si, do_copy=False, do_append=False)
+
+    def append_only(i):
+        gpu.layer = i % L
+        gpu.launch(si, do_decode=False, do_prefill=False)
+
+    ms_step = time_loop(torch, full_step, args.steps, args.warmup)
+    ms_decode = time_loop(torch, decode_only, args.steps, args.warmup)
+    ms_append = time_loop(torch, append_only, args.steps, args.warmup)
+    value = dbytes / (ms_step * 1e-3) / 1e9
+    achieved = dbytes / (ms_decode * 1e-3) / 1e9
+    plan_ws = pa.pa_decode_workspace_size(gpu.pool, len(lens), cfg["H_q"], int(lens.max()))
+    del gpu, si
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": "paged decode KV-read GB/s (% of HBM peak) + attention tokens/s at B=64",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen3-1.7b-shaped paged decode layer: append 32 + decode, B=32, GQA 16/8, head_dim 128, "
+                        "block 16, ctx U[512,640] (+1 appended), 1,378-block pool per layer, 28 layers rotated",
+            "B": 32, "H_q": 16, "H_kv": 8, "head_dim": 128, "block_size": 16, "pool_blocks": 1378,
+            "layers_rotated": L, "seed": 0,
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "decode_ms": round(ms_decode, 5),
+        "append_ms": round(ms_append, 5),
+        "decode_bytes": dbytes,
+        "decode_split_workspace_bytes": plan_ws,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "pa::decode_split_kernel<BF16,128,2,16> (+ merge when split)",
+            "per_launch_bytes": dbytes,
+        },
+    }
+
+    # ---------------------------------------------------------- B=64: config 3
+    scn3 = build_scenario(3, 0, bs=16)
+    g3 = GpuRun(scn3, device=dev, num_layers=1, fill="randn")
+    g3.run_setup()
+    si3 = g3.prepare(scn3.steps[0])
+    ms3 = time_loop(torch, lambda i: g3.launch(si3), max(20, args.steps // 4), 5)
+    ms3d = time_loop(torch, lambda i: g3.launch(si3, do_copy=False, do_append=False), max(20, args.steps // 4), 5)
+    lens3 = si3.lens.cpu().numpy()
+    b3 = decode_bytes(lens3, 40, 40, 128, 16, 2)
+    out["attention_tok_s_b64"] = round(64 / (ms3 * 1e-3), 1)
+    out["b64"] = {"workload": "13b-shaped MHA decode layer, B=64, 40 heads, block 16, lognormal ctx, churned pool",
+                  "ms_per_step": round(ms3, 5), "decode_ms": round(ms3d, 5),
+                  "decode_GBps": round(b3 / (ms3d * 1e-3) / 1e9, 1),
+                  "step_GBps": round(b3 / (ms3 * 1e-3) / 1e9, 1)}
+    del g3, si3
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------- other rows
+    if not args.no_rows:
+        rows = {}
+        scn4 = build_scenario(4, 0)
+        g4 = GpuRun(scn4, device=dev, fill="randn")
+        g4.run_setup()
+        tail = g4.prepare(scn4.steps[0])
+        dec = g4.prepare(scn4.steps[1])
+        nrep = 50
+        ms_copy = time_loop(torch, lambda i: g4.launch(tail, do_append=False), nrep, 5)
+        ms_tail = time_loop(torch, lambda i: g4.launch(tail, do_copy=False), nrep, 5)
+        ms_d4 = time_loop(torch, lambda i: g4.launch(dec, do_copy=False, do_append=False), nrep, 5)
+        L4 = dec.lens.cpu().numpy()
+        copy_b = 2 * tail.n_pairs * 1 * 2 * 8 * 16 * 128 * 2
+        uniq = 8 * 3000 * 8 * 128 * 2 * 2 + 64 * (int(L4[0]) - 3000) * 8 * 128 * 2 * 2
+        rows["cow_copy_blocks"] = {"workload": "shared-prefix sampling: 56 copy-on-write block copies",
+                                   "ms": round(ms_copy, 5), "GBps": round(copy_b / (ms_copy * 1e-3) / 1e9, 1)}
+        rows["append_2048"] = {"workload": "shared-prefix sampling: 64 x 32-token tails",
+                               "ms": round(ms_tail, 5),
+                               "GBps": round(append_bytes(2048, 8, 128, 2) / (ms_tail * 1e-3) / 1e9, 1)}
+        rows["decode_shared_prefix"] = {
+            "workload": "64 samples sharing 8 x 3,000-token prefixes, ctx 3,034",
+            "ms": round(ms_d4, 5),
+            "unique_GBps": round(uniq / (ms_d4 * 1e-3) / 1e9, 1),
+            "logical_GBps": round(decode_bytes(L4, 8, 32, 128, 16, 2) / (ms_d4 * 1e-3) / 1e9, 1)}
+        del g4, tail, dec
+        torch.cuda.empty_cache()
+
+        scn5 = build_scenario(5, 0)
+        g5 = GpuRun(scn5, device=dev, fill="randn")
+        g5.run_setup()
+        s5 = g5.prepare(scn5.steps[0])
+        ms_d5 = time_loop(torch, lambda i: g5.launch(s5, do_copy=False, do_append=False, do_prefill=False), 10, 2)
+        ms_p5 = time_loop(torch, lambda i: g5.launch(s5, do_copy=False, do_append=False, do_decode=False), 10, 2)
+        L5 = s5.lens.cpu().numpy()
+        fl = prefill_flops(1024, 64, 128, 3500)
+        rows["decode_long_ctx"] = {"workload": "63 sequences, ctx U[1024, 32768], GQA 64/8",
+                                   "ms": round(ms_d5, 5),
+                                   "GBps": round(decode_bytes(L5, 8, 64, 128, 16, 2) / (ms_d5 * 1e-3) / 1e9, 1)}
+        rows["prefill_chunk"] = {"workload": "1,024-token causal chunk after 3,500 cached tokens, GQA 64/8",
+                                 "ms": round(ms_p5, 5),
+                                 "TFLOPs": round(fl / (ms_p5 * 1e-3) / 1e12, 1),
+                                 "mfma_frac": round(fl / (ms_p5 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+        del g5, s5
+        torch.cuda.empty_cache()
+        out["rows"] = rows
+
+    # ---------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, dbytes)
+    out["wall_s"] = round(time.time() - t_start, 1)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(seconds, dbytes):
+    """The oracle on the same step (append 32 + decode of 32 sequences), timed
+    on this host's cores: repeated until ``seconds`` of work are done."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import attention, encoding
+    from oracle.run import OracleRun, widen
+    from pa_inputs import build_scenario
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        scn = build_scenario(2, 0)
+        orc = OracleRun(scn)
+        orc.run_setup()
+        st = scn.steps[0]
+        slots, _ = orc.bookkeeping(st)
+        cfg = scn.cfg
+        kb, vb = encoding.encode(st.k_new, "bf16"), encoding.encode(st.v_new, "bf16")
+        q = widen(st.q, "bf16")
+        tables = [orc.bm.block_table(s_) for s_ in st.decode_seqs]
+        lens = [orc.bm.seq_len(s_) for s_ in st.decode_seqs]
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            orc.pool.append(0, kb, vb, slots)
+            attention.decode(orc.pool, 0, q, tables, lens, cfg["scale"])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": round(dbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"the same decode step (append 32 + decode 32 sequences, float64 oracle) repeated {reps} "
+                      f"times in {el:.1f} s on {cores} visible host cores",
+            "ms_per_step": round(1e3 * el / reps, 3)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())
