@@ -35,52 +35,119 @@ namespace pa {
 
 constexpr float kNegInf = -INFINITY;
 
-template <typename E, int D, int BS>
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 0
+#endif
+
+// Unit = NLD wave loads of K and V (TPW tokens each).  Few query heads per
+// KV head: short units, 4 in flight per wave.  Many heads (more arithmetic
+// per byte): longer units for more independent work per lane, 2 in flight.
+template <typename E, int D, int BS, int G>
 struct DecodeShape {
   static constexpr int S = E::bytes;
-  static constexpr int VEC = 16 / S;                         // elements per lane chunk
-  static constexpr int LPT = D / VEC;                        // lanes per token row
-  static constexpr int TPW = 64 / LPT;                       // token rows per wave load
-  static constexpr int NLD = (BS / TPW) < 4 ? (BS / TPW) : 4;  // loads per unit per side
-  static constexpr int U = NLD * TPW;                        // tokens per unit
-  static constexpr int UPB = BS / U;                         // units per block
+  static constexpr int VEC = 16 / S;                             // elements per lane chunk
+  static constexpr int LPT = D / VEC;                            // lanes per token row
+  static constexpr int TPW = 64 / LPT;                           // token rows per wave load
+  static constexpr int NLD_MAX = G <= 2 ? 2 : 4;
+  static constexpr int NLD = (BS / TPW) < NLD_MAX ? (BS / TPW) : NLD_MAX;  // loads per unit per side
+  static constexpr int U = NLD * TPW;                            // tokens per unit
+  static constexpr int UPB = BS / U;                             // units per block
+  static constexpr int RING = G <= 2 ? 4 : 2;                    // units in flight per wave
   static_assert(BS % TPW == 0, "block size must hold whole wave loads");
   static_assert(BS % U == 0, "units tile a block");
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <typename E, int D, int G, int BS>
-__global__ void __launch_bounds__(512)
-    decode_split_kernel(const char* __restrict__ pool_k, const char* __restrict__ pool_v, int64_t layer_off,
-                        int64_t head_stride, const char* __restrict__ q, void* __restrict__ out,
-                        const int32_t* __restrict__ block_tables, int32_t max_blocks,
-                        const int32_t* __restrict__ context_lens, float scale_log2, int32_t H_q,
-                        int32_t blocks_per_part, int32_t num_parts, float* __restrict__ ws_ml,
-                        float* __restrict__ ws_acc) {
-  using Sh = DecodeShape<E, D, BS>;
-  constexpr int S = Sh::S, VEC = Sh::VEC, LPT = Sh::LPT, TPW = Sh::TPW, NLD = Sh::NLD, U = Sh::U,
-                UPB = Sh::UPB;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// q.k over one lane's 16-byte chunk.  The query is kept in its storage
+// format; bf16 and f16 pairs go through the packed dot instructions (exact
+// products, fp32 accumulate), fp32 through FMAs.
+template <typename E>
+struct QChunk;
+template <>
+struct QChunk<BF16> {
+  uint32_t w[4];
+  __device__ void set(const uint4& raw) { w[0] = raw.x, w[1] = raw.y, w[2] = raw.z, w[3] = raw.w; }
+  __device__ float dot(const uint4& k) const {
+    float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[0]), __builtin_bit_cast(bf16x2_t, k.x),
+                                              0.0f, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[1]), __builtin_bit_cast(bf16x2_t, k.y), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[2]), __builtin_bit_cast(bf16x2_t, k.z), d, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[3]), __builtin_bit_cast(bf16x2_t, k.w), d,
+                                           false);
+  }
+};
+template <>
+struct QChunk<F16> {
+  uint32_t w[4];
+  __device__ void set(const uint4& raw) { w[0] = raw.x, w[1] = raw.y, w[2] = raw.z, w[3] = raw.w; }
+  __device__ float dot(const uint4& k) const {
+    float d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w[0]), __builtin_bit_cast(f16x2_t, k.x), 0.0f, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w[1]), __builtin_bit_cast(f16x2_t, k.y), d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w[2]), __builtin_bit_cast(f16x2_t, k.z), d, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w[3]), __builtin_bit_cast(f16x2_t, k.w), d, false);
+  }
+};
+template <>
+struct QChunk<F32> {
+  float f[4];
+  __device__ void set(const uint4& raw) { widen(F32{}, raw, f); }
+  __device__ float dot(const uint4& k) const {
+    float kf[4];
+    widen(F32{}, k, kf);
+    float d = f[0] * kf[0];
+    d = fmaf(f[1], kf[1], d);
+    d = fmaf(f[2], kf[2], d);
+    return fmaf(f[3], kf[3], d);
+  }
+};
+
+
+template <typename E, int D, int G, int BS, int MAXT>
+__global__ void __launch_bounds__(MAXT)
+    decode_kernel(const char* __restrict__ pool_k, const char* __restrict__ pool_v, int64_t layer_off,
+                  int64_t head_stride, const char* __restrict__ q, void* __restrict__ out,
+                  const int32_t* __restrict__ block_tables, int32_t max_blocks,
+                  const int32_t* __restrict__ context_lens, float scale_log2, int32_t H_q, int32_t blocks_per_part,
+                  int32_t num_parts, float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
+  using Sh = DecodeShape<E, D, BS, G>;
+  constexpr int S = Sh::S, VEC = Sh::VEC, LPT = Sh::LPT, TPW = Sh::TPW, NLD = Sh::NLD, U = Sh::U, UPB = Sh::UPB,
+                RING = Sh::RING;
   extern __shared__ float smem[];
 
   const int part = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int W = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6;
+  // Wave-uniform by construction; readfirstlane lets the compiler keep the
+  // unit walk and the block-table reads in scalar registers / scalar loads,
+  // so that a table read never waits on the vector loads in flight.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane / LPT;  // token row inside a wave load
   const int c = lane % LPT;  // 16-byte chunk of the row
 
-  const int ctx = context_lens[b];
-  const int nblk = (ctx + BS - 1) / BS;
   const int j0 = part * blocks_per_part;
+  const int u_begin = j0 * UPB;
+  const int32_t* btrow = block_tables + static_cast<int64_t>(b) * max_blocks;
+  // Table entries of this wave's first RING units, read in parallel with the
+  // sequence length instead of after it (the index is clamped to the row; an
+  // entry past the sequence's end is simply not used).
+  int32_t ph[RING];
+#pragma unroll
+  for (int p = 0; p < RING; ++p)
+    ph[p] = max_blocks > 0 ? btrow[min((u_begin + wave + p * W) / UPB, max_blocks - 1)] : 0;
+  const int ctx = __builtin_amdgcn_readfirstlane(context_lens[b]);
+  const int nblk = (ctx + BS - 1) / BS;
   const int64_t head0 = static_cast<int64_t>(b) * H_q + static_cast<int64_t>(g) * G;
 
   if (j0 >= nblk) {
     // Nothing visible in this partition.  With a single partition that means
     // an empty sequence: its rows are zeros.  Split partitions past the end
-    // are never read by the merge.
+    // are not counted by the merge.
     if (num_parts == 1) {
       for (int i = threadIdx.x; i < G * D; i += blockDim.x) store_elem(E{}, out, head0 * D + i, 0.0f);
     }
@@ -88,15 +155,9 @@ __global__ void __launch_bounds__(512)
   }
   const int j1 = min(j0 + blocks_per_part, nblk);
 
-  // q of the G heads for this lane's chunk, pre-multiplied by scale*log2(e).
-  float qf[G][VEC];
+  QChunk<E> qc[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    uint4 raw = load16(q + ((head0 + h) * D + c * VEC) * S);
-    widen(E{}, raw, qf[h]);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) qf[h][e] *= scale_log2;
-  }
+  for (int h = 0; h < G; ++h) qc[h].set(load16(q + ((head0 + h) * D + c * VEC) * S));
 
   float m[G], l[G], acc[G][VEC];
 #pragma unroll
@@ -109,53 +170,63 @@ __global__ void __launch_bounds__(512)
 
   const char* kbase = pool_k + layer_off + static_cast<int64_t>(g) * head_stride;
   const char* vbase = pool_v + layer_off + static_cast<int64_t>(g) * head_stride;
-  const int32_t* btrow = block_tables + static_cast<int64_t>(b) * max_blocks;
-  const int lane_off = (r * D + c * VEC) * S;  // inside a unit, for load 0
+  const int lane_off = (r * D + c * VEC) * S;
 
-  auto load_unit = [&](int u, uint4* kr, uint4* vr) {
-    const int blk = u / UPB;
-    const int sub = u % UPB;
-    const int64_t phys = btrow[blk];
-    const int64_t off = (phys * BS + sub * U) * static_cast<int64_t>(D * S) + lane_off;
+  auto load_unit = [&](int u, uint4* kr, uint4* vr, int32_t phys_id) {
+    const int64_t phys = __builtin_amdgcn_readfirstlane(phys_id);
+    const int64_t off = (phys * BS + (u % UPB) * U) * static_cast<int64_t>(D * S) + lane_off;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
+#if PA_DECODE_NT
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off + i * TPW * D * S));
+      const u32x4 bb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off + i * TPW * D * S));
+      kr[i] = make_uint4(a.x, a.y, a.z, a.w);
+      vr[i] = make_uint4(bb.x, bb.y, bb.z, bb.w);
+#else
       kr[i] = load16(kbase + off + i * TPW * D * S);
       vr[i] = load16(vbase + off + i * TPW * D * S);
+#endif
     }
   };
 
+  // One unit: NLD tokens per lane row, online-softmax update for G heads.
   auto process = [&](int u, const uint4* kr, const uint4* vr, bool masked) {
-    const int tok0 = u * U + r;  // this lane's first token of the unit
+    const int tok0 = u * U + r;
     float s[NLD][G];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      float kf[VEC];
-      widen(E{}, kr[i], kf);
+      const bool dead = masked && tok0 + i * TPW >= ctx;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float d = 0.0f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) d = fmaf(qf[h][e], kf[e], d);
-        s[i][h] = group_sum<LPT>(d);
+        const float d = group_sum<LPT>(qc[h].dot(kr[i])) * scale_log2;
+        s[i][h] = dead ? kNegInf : d;
       }
-      if (masked && tok0 + i * TPW >= ctx) {
+    }
+    // Running max: rescale (l, acc) only when some lane's max grew, which
+    // after the first few units of a sequence is rare.
+    float mx[G];
+    bool grew = false;
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
+    for (int h = 0; h < G; ++h) {
+      mx[h] = m[h];
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) mx[h] = fmaxf(mx[h], s[i][h]);
+      grew |= mx[h] > m[h];
+    }
+    if (__any(grew)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float alpha = exp2_fast(m[h] - ((mx[h] == kNegInf) ? 0.0f : mx[h]));
+        m[h] = mx[h];
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
       }
     }
     float msafe[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = m[h];
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) mx = fmaxf(mx, s[i][h]);
-      msafe[h] = (mx == kNegInf) ? 0.0f : mx;
-      const float alpha = exp2_fast(m[h] - msafe[h]);
-      m[h] = mx;
-      l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
-    }
+    for (int h = 0; h < G; ++h) msafe[h] = (m[h] == kNegInf) ? 0.0f : m[h];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       float vf[VEC];
@@ -175,26 +246,49 @@ __global__ void __launch_bounds__(512)
     }
   };
 
-  const int u_end = j1 * UPB;
-  int u = j0 * UPB + wave;
-  uint4 kc[NLD], vc[NLD];
-  if (u < u_end) load_unit(u, kc, vc);
-  while (u < u_end) {
-    const int un = u + W;
-    uint4 kn[NLD], vn[NLD];
-    if (un < u_end) load_unit(un, kn, vn);
-    const bool masked = (u + 1) * U > ctx;
-    if (masked)
-      process(u, kc, vc, true);
-    else
-      process(u, kc, vc, false);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      kc[i] = kn[i];
-      vc[i] = vn[i];
-    }
-    u = un;
+  // Units of this partition: full ones [u_first, u_full), stepping by W per
+  // wave, streamed through a ring of RING loads in flight; then at most one
+  // partly visible unit, handled by the wave that owns it.
+  const int u_stop = min(j1 * UPB, (ctx + U - 1) / U);
+  const int u_full = min(u_stop, ctx / U);
+  const int u_first = u_begin + wave;
+  const int n_w = u_full > u_first ? (u_full - u_first + W - 1) / W : 0;  // this wave's full units
+  // The partly visible last unit (if this partition has it) is loaded first,
+  // by the wave it falls to, and processed last with masking.
+  const bool has_tail = u_full < u_stop && u_full >= u_first && (u_full - u_first) % W == 0;
+  uint4 kt[NLD], vt[NLD];
+  {
+    // Unconditional (a wave without the tail re-reads its partition's first
+    // unit, a cache hit): every wave then has the same loads in flight, and
+    // the waits below stay exact instead of draining the whole ring.
+    const int ut = has_tail ? u_full : u_begin;
+    load_unit(ut, kt, vt, btrow[ut / UPB]);
   }
+  if (n_w > 0) {
+    // Refills are unconditional, with the unit index clamped to the wave's
+    // last one (a cache hit), so each ring slot stays in fixed registers and
+    // no load ever waits for a later one.
+    uint4 kr[RING][NLD], vr[RING][NLD];
+#pragma unroll
+    for (int p = 0; p < RING; ++p) {
+      const int u = u_first + min(p, n_w - 1) * W;
+      load_unit(u, kr[p], vr[p], p < n_w ? ph[p] : btrow[u / UPB]);
+    }
+    for (int k = 0; k < n_w; k += RING) {
+#pragma unroll
+      for (int p = 0; p < RING; ++p) {
+        const int idx = k + p;
+        if (idx < n_w) process(u_first + idx * W, kr[p], vr[p], false);
+        // Keep refills in ring order: the in-order load counter then only
+        // ever waits for the oldest slot.
+        __builtin_amdgcn_sched_barrier(0);
+        const int un = u_first + min(idx + RING, n_w - 1) * W;
+        load_unit(un, kr[p], vr[p], btrow[un / UPB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if (has_tail) process(u_full, kt, vt, true);
 
   // Merge the TPW row groups of this wave (lanes LPT, 2*LPT, ... apart hold
   // the same dims of different tokens).
@@ -262,11 +356,14 @@ __global__ void __launch_bounds__(512)
 
 // Combines the partitions of each (sequence, query head):
 // out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), M = max_p m_p.
+// The (m, l) of all partitions are staged in LDS once; each thread then sums
+// its dimension over the partitions with several loads in flight.
 template <typename E, int D>
 __global__ void __launch_bounds__(D)
     decode_merge_kernel(void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
                         const int32_t* __restrict__ context_lens, int32_t H_q, int32_t num_parts,
                         int32_t part_tokens) {
+  extern __shared__ float w_lds[];  // [num_parts] weights, then [1] total
   const int64_t bh = blockIdx.x;
   const int b = static_cast<int>(bh / H_q);
   const int e = threadIdx.x;
@@ -275,14 +372,35 @@ __global__ void __launch_bounds__(D)
   const float* ml = ws_ml + bh * num_parts * 2;
   const float* ac = ws_acc + bh * num_parts * D;
   float mx = kNegInf;
-  for (int p = 0; p < np; ++p) mx = fmaxf(mx, ml[2 * p]);
+  for (int p = e; p < np; p += D) mx = fmaxf(mx, ml[2 * p]);
+  // block max over D threads (D = 64 or 128: one or two waves)
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  __shared__ float red[2];
+  if ((e & 63) == 0) red[e >> 6] = mx;
+  __syncthreads();
+  mx = D > 64 ? fmaxf(red[0], red[1]) : red[0];
   const float ms = (mx == kNegInf) ? 0.0f : mx;
-  float lt = 0.0f, at = 0.0f;
-  for (int p = 0; p < np; ++p) {
+  float lsum = 0.0f;
+  for (int p = e; p < np; p += D) {
     const float wt = exp2_fast(ml[2 * p] - ms);
-    lt += ml[2 * p + 1] * wt;
-    at += ac[p * D + e] * wt;
+    w_lds[p] = wt;
+    lsum += ml[2 * p + 1] * wt;
   }
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
+  __syncthreads();
+  if ((e & 63) == 0) red[e >> 6] = lsum;
+  __syncthreads();
+  const float lt = D > 64 ? red[0] + red[1] : red[0];
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  int p = 0;
+  for (; p + 3 < np; p += 4) {
+    a0 += ac[(p + 0) * D + e] * w_lds[p + 0];
+    a1 += ac[(p + 1) * D + e] * w_lds[p + 1];
+    a2 += ac[(p + 2) * D + e] * w_lds[p + 2];
+    a3 += ac[(p + 3) * D + e] * w_lds[p + 3];
+  }
+  for (; p < np; ++p) a0 += ac[p * D + e] * w_lds[p];
+  const float at = (a0 + a1) + (a2 + a3);
   store_elem(E{}, out, bh * D + e, lt > 0.0f ? at / lt : 0.0f);
 }
 
@@ -300,64 +418,98 @@ static int env_int(const char* name, int dflt) {
   return std::atoi(s);
 }
 
-// Grid plan from host-side sizes only (context lengths stay on the device):
-// aim for about 4 workgroups per CU, never fewer than ~2 blocks per wave.
-static DecodePlan plan_decode(int B, int H_kv, int bs, int max_ctx) {
-  // Tuning overrides, read on every call so that a process can sweep them.
+template <int G>
+constexpr int max_threads() {
+  return G <= 2 ? 1024 : 512;
+}
+
+static int max_waves_for(int G) { return (G <= 2 ? 1024 : 512) / 64; }
+
+// Grid plan from host-side sizes only (context lengths stay on the device).
+// Tuning overrides PA_DECODE_WAVES / PA_DECODE_PART_BLOCKS are read on every
+// call so that one process can sweep them.
+static DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx) {
   const int env_waves = env_int("PA_DECODE_WAVES", 0);
   const int env_pb = env_int("PA_DECODE_PART_BLOCKS", 0);
   DecodePlan p;
   const int64_t nblk = ceil_div(max_ctx > 0 ? max_ctx : 1, bs);
   const int64_t pairs = static_cast<int64_t>(B) * H_kv;
-  p.waves = env_waves > 0 ? env_waves : 4;
-  if (p.waves > 8) p.waves = 8;
+  p.waves = env_waves > 0 ? env_waves : 8;
+  p.waves = p.waves > max_waves_for(G) ? max_waves_for(G) : p.waves;
   if (env_pb > 0) {
     p.blocks_per_part = env_pb;
+  } else if (pairs >= 256 && nblk <= 256) {
+    // Enough (sequence, kv head) pairs to fill the chip and contexts short
+    // enough that one workgroup per pair finishes in a few tens of
+    // microseconds: a split would only add merge latency.
+    p.blocks_per_part = static_cast<int>(nblk);
   } else {
-    const int64_t target_wgs = 1024;
-    int64_t parts = ceil_div(target_wgs, pairs);
-    const int64_t min_pb = 2 * p.waves;
-    const int64_t max_parts = ceil_div(nblk, min_pb);
-    if (parts > max_parts) parts = max_parts;
-    if (parts < 1) parts = 1;
-    p.blocks_per_part = static_cast<int>(ceil_div(nblk, parts));
+    // Long contexts or few pairs: cut each sequence into partitions of at
+    // least 64 blocks, enough that the hardware can balance ~4 per CU.
+    const int64_t parts = ceil_div(4 * 256, pairs);
+    int64_t pb = ceil_div(nblk, parts);
+    if (pb < 64) pb = 64;
+    p.blocks_per_part = static_cast<int>(pb);
   }
   p.num_parts = static_cast<int>(ceil_div(nblk, p.blocks_per_part));
   return p;
 }
 
+// Workspace of a split decode: (m, l) partials [B][H_q][P][2], then the
+// un-normalised weighted V sums [B][H_q][P][D], fp32.
+struct Workspace {
+  float* ml;
+  float* acc;
+};
+
+static size_t workspace_bytes_for(const DecodePlan& pl, int B, int H_kv, int H_q, int D) {
+  if (pl.num_parts <= 1) return 0;
+  (void)H_kv;
+  return static_cast<size_t>(B) * H_q * pl.num_parts * (D + 2) * sizeof(float);
+}
+
+static Workspace carve(void* ws, const DecodePlan& pl, int B, int H_kv, int H_q) {
+  Workspace w{nullptr, nullptr};
+  (void)H_kv;
+  if (pl.num_parts <= 1) return w;
+  w.ml = static_cast<float*>(ws);
+  w.acc = w.ml + static_cast<size_t>(B) * H_q * pl.num_parts * 2;
+  return w;
+}
+
 template <typename E, int D, int G, int BS>
-static void launch_split(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B, int32_t H_q,
-                         const int32_t* bt, int32_t max_blocks, const int32_t* ctx, float scale_log2,
-                         const DecodePlan& pl, float* ws_ml, float* ws_acc, hipStream_t stream) {
+static void launch_decode(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B, int32_t H_q,
+                          const int32_t* bt, int32_t max_blocks, const int32_t* ctx, float scale_log2,
+                          const DecodePlan& pl, const Workspace& ws, hipStream_t stream) {
   const int64_t head_stride = static_cast<int64_t>(pool->num_blocks) * BS * D * E::bytes;
   const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * head_stride;
   const size_t lds = static_cast<size_t>(pl.waves) * G * (D + 2) * sizeof(float);
   dim3 grid(pl.num_parts, pool->num_kv_heads, B);
-  hipLaunchKernelGGL((decode_split_kernel<E, D, G, BS>), grid, dim3(64 * pl.waves), lds, stream,
+  hipLaunchKernelGGL((decode_kernel<E, D, G, BS, max_threads<G>()>), grid, dim3(64 * pl.waves), lds, stream,
                      static_cast<const char*>(pool->k), static_cast<const char*>(pool->v), layer_off, head_stride,
                      static_cast<const char*>(q), out, bt, max_blocks, ctx, scale_log2, H_q, pl.blocks_per_part,
-                     pl.num_parts, ws_ml, ws_acc);
+                     pl.num_parts, ws.ml, ws.acc);
   if (pl.num_parts > 1) {
-    hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(static_cast<uint32_t>(B) * H_q), dim3(D), 0, stream, out,
-                       ws_ml, ws_acc, ctx, H_q, pl.num_parts, pl.blocks_per_part * BS);
+    hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(static_cast<uint32_t>(B) * H_q), dim3(D),
+                       pl.num_parts * sizeof(float), stream, out, ws.ml, ws.acc, ctx, H_q, pl.num_parts,
+                       pl.blocks_per_part * BS);
   }
 }
 
-using SplitFn = void (*)(const pa_kv_pool*, int32_t, void*, const void*, int32_t, int32_t, const int32_t*, int32_t,
-                         const int32_t*, float, const DecodePlan&, float*, float*, hipStream_t);
+using DecodeFn = void (*)(const pa_kv_pool*, int32_t, void*, const void*, int32_t, int32_t, const int32_t*, int32_t,
+                          const int32_t*, float, const DecodePlan&, const Workspace&, hipStream_t);
 
 template <typename E, int D, int G>
-static SplitFn pick_bs(int bs) {
+static DecodeFn pick_bs(int bs) {
   switch (bs) {
-    case 8: return &launch_split<E, D, G, 8>;
-    case 16: return &launch_split<E, D, G, 16>;
-    case 32: return &launch_split<E, D, G, 32>;
+    case 8: return &launch_decode<E, D, G, 8>;
+    case 16: return &launch_decode<E, D, G, 16>;
+    case 32: return &launch_decode<E, D, G, 32>;
   }
   return nullptr;
 }
 template <typename E, int D>
-static SplitFn pick_g(int G, int bs) {
+static DecodeFn pick_g(int G, int bs) {
   switch (G) {
     case 1: return pick_bs<E, D, 1>(bs);
     case 2: return pick_bs<E, D, 2>(bs);
@@ -367,25 +519,20 @@ static SplitFn pick_g(int G, int bs) {
   return nullptr;
 }
 template <typename E>
-static SplitFn pick_d(int D, int G, int bs) {
+static DecodeFn pick_d(int D, int G, int bs) {
   switch (D) {
     case 64: return pick_g<E, 64>(G, bs);
     case 128: return pick_g<E, 128>(G, bs);
   }
   return nullptr;
 }
-static SplitFn pick(int dtype, int D, int G, int bs) {
+static DecodeFn pick(int dtype, int D, int G, int bs) {
   switch (dtype) {
     case PA_F32: return pick_d<F32>(D, G, bs);
     case PA_BF16: return pick_d<BF16>(D, G, bs);
     case PA_F16: return pick_d<F16>(D, G, bs);
   }
   return nullptr;
-}
-
-static size_t workspace_bytes_for(const DecodePlan& pl, int B, int H_q, int D) {
-  if (pl.num_parts <= 1) return 0;
-  return static_cast<size_t>(B) * H_q * pl.num_parts * (D + 2) * sizeof(float);
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -395,8 +542,9 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 extern "C" size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t B, int32_t H_q, int32_t max_ctx) {
   using namespace pa;
   if (!pool || B <= 0 || H_q <= 0 || pool->block_size <= 0 || pool->num_kv_heads <= 0) return 0;
-  DecodePlan pl = plan_decode(B, pool->num_kv_heads, pool->block_size, max_ctx);
-  return workspace_bytes_for(pl, B, H_q, pool->head_dim);
+  if (H_q % pool->num_kv_heads) return 0;
+  DecodePlan pl = plan_decode(B, pool->num_kv_heads, H_q / pool->num_kv_heads, pool->block_size, max_ctx);
+  return workspace_bytes_for(pl, B, pool->num_kv_heads, H_q, pool->head_dim);
 }
 
 extern "C" int pa_decode(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B, int32_t H_q,
@@ -415,15 +563,16 @@ extern "C" int pa_decode(const pa_kv_pool* pool, int32_t layer, void* out, const
     return fail(PA_EINVAL, "pa_decode: q and pool must be 16-byte aligned");
   if (B > 65535 || pool->num_kv_heads > 65535) return fail(PA_EINVAL, "pa_decode: grid too large");
   const int G = H_q / pool->num_kv_heads;
-  SplitFn fn = pick(pool->dtype, pool->head_dim, G, pool->block_size);
+  DecodeFn fn = pick(pool->dtype, pool->head_dim, G, pool->block_size);
   if (!fn) return fail(PA_ENOTSUP, "pa_decode: (dtype, head_dim, block_size, H_q/H_kv) not compiled");
-  DecodePlan pl = plan_decode(B, pool->num_kv_heads, pool->block_size, max_ctx);
-  const size_t need = workspace_bytes_for(pl, B, H_q, pool->head_dim);
+  DecodePlan pl = plan_decode(B, pool->num_kv_heads, G, pool->block_size, max_ctx);
+  const size_t need = workspace_bytes_for(pl, B, pool->num_kv_heads, H_q, pool->head_dim);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_ESPACE, "pa_decode: workspace of " + std::to_string(need) + " bytes needed");
-  float* ws_ml = static_cast<float*>(workspace);
-  float* ws_acc = need ? ws_ml + static_cast<size_t>(B) * H_q * pl.num_parts * 2 : nullptr;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u))
+    return fail(PA_EINVAL, "pa_decode: workspace must be 4-byte aligned");
+  Workspace ws = carve(workspace, pl, B, pool->num_kv_heads, H_q);
   const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  fn(pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens, scale_log2, pl, ws_ml, ws_acc, stream);
+  fn(pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens, scale_log2, pl, ws, stream);
   return check_launch("pa_decode");
 }

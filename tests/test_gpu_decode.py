@@ -269,3 +269,55 @@ def test_decode_large_batch_and_long_context():
     out = f64(_gpu_decode(gp, q32, tables, lengths, 0.088, "bf16"))
     ref = attention.decode(op, 0, widen(q32, "bf16"), tables, lengths, 0.088)
     assert max_abs_err(out, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("plan", [(8, 4), (4, 1), (16, 3)])
+def test_decode_graph_replay_matches_eager(plan, monkeypatch):
+    """Split decodes captured in one graph (several launches sharing one
+    workspace) give the eager result on every replay, with eager work and
+    synchronisation between replays."""
+    from paged_kv_cache_140_amd import decode_workspace, pa_decode
+    from paged_kv_cache_140_amd.runner import to_device
+
+    monkeypatch.setenv("PA_DECODE_WAVES", str(plan[0]))
+    monkeypatch.setenv("PA_DECODE_PART_BLOCKS", str(plan[1]))
+    rng = np.random.default_rng(6)
+    lengths = [513, 640, 1, 77, 300]
+    H_q, H_kv, d, bs = 16, 8, 128, 16
+    op, gp, tables = _world(rng, lengths, H_q, H_kv, d, bs, "bf16", poison=False)
+    B = len(lengths)
+    maxb = max(len(t) for t in tables)
+    tab = np.zeros((B, maxb), dtype=np.int32)
+    for i, t in enumerate(tables):
+        tab[i, :len(t)] = t
+    tab_d = torch.from_numpy(tab).cuda()
+    lens_d = torch.tensor(lengths, dtype=torch.int32).cuda()
+    qs = [to_device(rng.standard_normal((B, H_q, d)).astype(np.float32), "bf16", "cuda") for _ in range(3)]
+    outs = [torch.empty_like(q) for q in qs]
+    ws = decode_workspace(gp, B, H_q, max(lengths))
+    say("decode graph replay", plan)
+
+    def run_all():
+        for q, o in zip(qs, outs):
+            pa_decode(gp, 0, o, q, tab_d, lens_d, max(lengths), 0.09, ws)
+
+    run_all()
+    torch.cuda.synchronize()
+    eager = [bits(o) for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert np.array_equal(bits(o), e), f"replay {rep} differs"
+        run_all()  # eager work between replays
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert np.array_equal(bits(o), e)
+    ref = attention.decode(op, 0, widen(np.zeros((B, H_q, d), np.float32), "bf16"), tables, lengths, 0.09)
+    del ref, g
