@@ -55,6 +55,12 @@ struct Mfma<F16> {
 };
 
 constexpr int kPrefillThreads = 256;
+
+// Byte column inside a V^T row, XOR-swizzled by the dim's 8-row group so that
+// the 16 lanes staging one key quad (dims 8 apart, rows 1,152 B apart) spread
+// over 8 bank groups instead of one; 16-byte chunks stay intact, so operand
+// reads apply the same map to their chunk start.
+__device__ __forceinline__ int vt_col(int dim, int colbyte) { return colbyte ^ (((dim >> 3) & 7) << 4); }
 constexpr int kKeysPerStep = 64;
 
 template <typename E, int D, int G, int BS>
@@ -78,6 +84,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
 
   __shared__ __attribute__((aligned(16))) char lds_k[2][KT * KROW];
   __shared__ __attribute__((aligned(16))) char lds_v[2][D * VROW];
+  extern __shared__ int32_t s_table[];  // [ceil(keys needed / BS)]
 
   const int g = blockIdx.y;
   const int t0 = blockIdx.x * TP;
@@ -86,7 +93,6 @@ __global__ void __launch_bounds__(kPrefillThreads)
   const int lane = tid & 63;
   const int li = lane & 15;
   const int lg = lane >> 4;
-  const int ctx_total = ctx_before + T;
   const int t_last = min(t0 + TP, T) - 1;
   const int kmax = ctx_before + t_last + 1;
   const int nsteps = (kmax + KT - 1) / KT;
@@ -130,16 +136,18 @@ __global__ void __launch_bounds__(kPrefillThreads)
   uint4 vst[VPT][4];
 
   auto key_addr = [&](const char* base, int key, int dchunk) -> const char* {
-    const int64_t phys = table[key / BS];
+    const int64_t phys = s_table[key / BS];
     return base + (phys * BS + key % BS) * static_cast<int64_t>(D * 2) + dchunk * 16;
   };
+  // Gathers stop at kmax: no row of this workgroup sees a later key (those
+  // tiles are zero-filled), and s_table holds exactly the entries below it.
   auto gload = [&](int step) {
     const int key0 = step * KT;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + i * kPrefillThreads;
       const int key = key0 + c / DCH;
-      kst[i] = key < ctx_total ? load16(key_addr(kbase, key, c % DCH)) : make_uint4(0, 0, 0, 0);
+      kst[i] = key < kmax ? load16(key_addr(kbase, key, c % DCH)) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -148,7 +156,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
         const int keyq = key0 + (u / DCH) * 4;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          vst[i][j] = keyq + j < ctx_total ? load16(key_addr(vbase, keyq + j, u % DCH)) : make_uint4(0, 0, 0, 0);
+          vst[i][j] = keyq + j < kmax ? load16(key_addr(vbase, keyq + j, u % DCH)) : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -176,11 +184,18 @@ __global__ void __launch_bounds__(kPrefillThreads)
           const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xFFFFu, a3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
           uint2 pk = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
           const int dim = (u % DCH) * 8 + e;
-          *reinterpret_cast<uint2*>(&lds_v[buf][dim * VROW + pos * 2]) = pk;
+          *reinterpret_cast<uint2*>(&lds_v[buf][dim * VROW + vt_col(dim, pos * 2)]) = pk;
         }
       }
     }
   };
+
+  // The workgroup's slice of the block table, staged once: the per-step
+  // gathers then find physical blocks in LDS instead of waiting on a global
+  // load before every K/V load.
+  const int nblk_used = (kmax + BS - 1) / BS;
+  for (int i = tid; i < nblk_used; i += kPrefillThreads) s_table[i] = table[i];
+  __syncthreads();
 
   gload(0);
   lds_store(0);
@@ -256,7 +271,8 @@ __global__ void __launch_bounds__(kPrefillThreads)
     for (int kk = 0; kk < KT / 32; ++kk) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const vec a = *reinterpret_cast<const vec*>(&lds_v[buf][(dt * 16 + li) * VROW + (kk * 32 + lg * 8) * 2]);
+        const int dim = dt * 16 + li;
+        const vec a = *reinterpret_cast<const vec*>(&lds_v[buf][dim * VROW + vt_col(dim, (kk * 32 + lg * 8) * 2)]);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) o[rt][dt] = M::mma(a, pb[rt][kk], o[rt][dt]);
       }
@@ -297,7 +313,8 @@ static void launch_prefill(const pa_kv_pool* pool, int32_t layer, void* out, con
   const int64_t head_stride = static_cast<int64_t>(pool->num_blocks) * BS * D * 2;
   const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * head_stride;
   dim3 grid(static_cast<uint32_t>((T + TP - 1) / TP), pool->num_kv_heads);
-  hipLaunchKernelGGL((prefill_chunk_kernel<E, D, G, BS>), grid, dim3(kPrefillThreads), 0, stream,
+  const size_t table_lds = static_cast<size_t>((static_cast<int64_t>(ctx_before) + T + BS - 1) / BS) * sizeof(int32_t);
+  hipLaunchKernelGGL((prefill_chunk_kernel<E, D, G, BS>), grid, dim3(kPrefillThreads), table_lds, stream,
                      static_cast<const char*>(pool->k), static_cast<const char*>(pool->v), layer_off, head_stride,
                      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), table, T, H_q, ctx_before,
                      scale_log2);
@@ -349,6 +366,9 @@ extern "C" int pa_prefill_chunk(const pa_kv_pool* pool, int32_t layer, void* out
        reinterpret_cast<uintptr_t>(pool->v)) & 15u)
     return fail(PA_EINVAL, "pa_prefill_chunk: q, out and pool must be 16-byte aligned");
   if (pool->num_kv_heads > 65535) return fail(PA_EINVAL, "pa_prefill_chunk: grid too large");
+  // The kernel keeps its slice of the block table in LDS next to ~70 KB of K/V tiles.
+  if (ceil_div(total, pool->block_size) * 4 > 64 * 1024)
+    return fail(PA_ENOTSUP, "pa_prefill_chunk: ctx_before + T needs more than 16,384 table entries");
   const int G = H_q / pool->num_kv_heads;
   PrefillFn fn = nullptr;
   if (pool->dtype == PA_BF16) fn = prefill_d<BF16>(pool->head_dim, G, pool->block_size);
