@@ -10,19 +10,23 @@
 //
 // How: QK^T and PV are dense contractions, so they run on bf16/f16 MFMA
 // (v_mfma_f32_16x16x32_{bf16,f16}) with fp32 accumulation.
-//  * workgroup = 4 waves = 128 query rows of one KV head: TP = 128/G
+//  * workgroup = 8 waves x 16 query rows of one KV head: TP = 128/G
 //    positions x the G query heads that share the KV head, so every K/V tile
 //    staged in LDS serves all G heads.  Row r is (position r / G, head r % G).
-//  * keys advance 64 at a time.  The tile is gathered block by block through
-//    the table into double-buffered LDS: K row-major (padded rows), V
-//    transposed with a key order that makes each lane's PV operand one
-//    16-byte read.
+//    16 rows per wave keep the kernel near 160 VGPRs, so several workgroups
+//    share a CU and hide each other's LDS and exp latency.
+//  * keys advance 64 at a time.  The tile is gathered through the table
+//    (staged once in LDS) into double-buffered LDS, K and V both row-major
+//    with an XOR swizzle of the 16-byte chunks that keeps MFMA operand reads
+//    and transposing reads free of bank conflicts beyond 2-way.
 //  * S^T = K Q^T is computed (keys on the MFMA row axis), so the fp32 result
 //    a lane holds -- 4 keys of one query row per 16x16 tile -- is, after the
 //    softmax, exactly its B operand of O^T += V^T P^T: P never leaves
-//    registers.
-//  * online softmax in the log2 domain; the causal mask is applied only in
-//    the last steps, whose keys can pass a row's position.
+//    registers.  The V^T operand comes from two ds_read_b64_tr_b16 reads.
+//  * online softmax in the log2 domain with the scale folded into the
+//    exponent; the running output is rescaled only when a row's maximum
+//    grows, and the causal mask is applied only in the last steps, whose keys
+//    can pass a row's position.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -54,14 +58,32 @@ struct Mfma<F16> {
   __device__ static uint16_t cvt(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
 };
 
-constexpr int kPrefillThreads = 256;
-
-// Byte column inside a V^T row, XOR-swizzled by the dim's 8-row group so that
-// the 16 lanes staging one key quad (dims 8 apart, rows 1,152 B apart) spread
-// over 8 bank groups instead of one; 16-byte chunks stay intact, so operand
-// reads apply the same map to their chunk start.
-__device__ __forceinline__ int vt_col(int dim, int colbyte) { return colbyte ^ (((dim >> 3) & 7) << 4); }
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kKeysPerStep = 64;
+
+// 16-byte chunk position of (key, chunk) inside a K or V tile row in LDS.
+// Rows are stored unpadded; the XOR keeps the 16 rows one MFMA operand read
+// touches -- and the 4 rows x 2 chunks one transposing read touches -- on
+// distinct bank groups.
+template <int DCH>
+__device__ __forceinline__ int swz(int key, int chunk) {
+  if constexpr (DCH >= 16)
+    return chunk ^ ((2 * (key & 7) + ((key >> 3) & 1)) & (DCH - 1));
+  else
+    return chunk ^ ((key >> 1) & (DCH - 1));
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane 4k+q supplies the address of 4 consecutive 16-bit elements and
+// lane 4q+e receives element e of lanes q, 4+q, 8+q, 12+q.
+__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
+  const v4i16_t v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 template <typename E, int D, int G, int BS>
 __global__ void __launch_bounds__(kPrefillThreads)
@@ -71,19 +93,22 @@ __global__ void __launch_bounds__(kPrefillThreads)
                          float scale_log2) {
   using M = Mfma<E>;
   using vec = typename M::vec;
-  constexpr int TP = 128 / G;       // positions per workgroup
-  constexpr int KT = kKeysPerStep;  // keys per step
-  constexpr int RT = 2;             // 16-row tiles per wave
-  constexpr int KS = D / 32;        // MFMA k-steps over the head dim
-  constexpr int DT = D / 16;        // 16-dim output tiles
-  constexpr int KROW = D * 2 + 16;  // LDS bytes per K row (padded against bank conflicts)
-  constexpr int VROW = KT * 2 + 16; // LDS bytes per V^T row
-  constexpr int DCH = D / 8;        // 16-byte chunks per K/V row
-  static_assert(128 % G == 0, "query group must divide 128 rows");
+  constexpr int ROWS = 16 * kPrefillWaves;  // query rows per workgroup, 16 per wave
+  constexpr int TP = ROWS / G;              // positions per workgroup
+  constexpr int KT = kKeysPerStep;          // keys per step
+  constexpr int KS = D / 32;                // MFMA k-steps over the head dim
+  constexpr int DT = D / 16;                // 16-dim output tiles
+  constexpr int NT = KT / 16;               // 16-key score tiles per step
+  constexpr int KK = KT / 32;               // 32-key PV k-steps per step
+  constexpr int ROWB = D * 2;               // bytes per K/V row in LDS
+  constexpr int DCH = D / 8;                // 16-byte chunks per row
+  constexpr int CPT = KT * DCH / kPrefillThreads;  // chunks per thread per side per step
+  static_assert(ROWS % G == 0, "query group must divide the workgroup's rows");
   static_assert(KT % BS == 0 || BS % KT == 0, "steps align with blocks");
+  static_assert(CPT >= 1 && KT * DCH % kPrefillThreads == 0, "staging covers the tile");
 
-  __shared__ __attribute__((aligned(16))) char lds_k[2][KT * KROW];
-  __shared__ __attribute__((aligned(16))) char lds_v[2][D * VROW];
+  __shared__ __attribute__((aligned(16))) char lds_k[2][KT * ROWB];
+  __shared__ __attribute__((aligned(16))) char lds_v[2][KT * ROWB];
   extern __shared__ int32_t s_table[];  // [ceil(keys needed / BS)]
 
   const int g = blockIdx.y;
@@ -94,108 +119,65 @@ __global__ void __launch_bounds__(kPrefillThreads)
   const int li = lane & 15;
   const int lg = lane >> 4;
   const int t_last = min(t0 + TP, T) - 1;
-  const int kmax = ctx_before + t_last + 1;
+  const int kmax = ctx_before + t_last + 1;  // no row of this workgroup sees key kmax or later
   const int nsteps = (kmax + KT - 1) / KT;
-  const int first_masked_key = ctx_before + t0 + 1;  // keys beyond this may be masked for some row
+  const int first_masked_key = ctx_before + t0 + 1;
 
-  // Query rows of this lane (as the MFMA B operand) and their key limits.
-  vec qb[RT][KS];
-  int limit[RT];
+  // This lane's query row (MFMA B operand) and its last visible key.
+  vec qb[KS];
+  const int r = wave * 16 + li;
+  const int pos = t0 + r / G;
+  const int limit = ctx_before + pos;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = wave * 32 + rt * 16 + li;
-    const int pos = t0 + r / G;
-    const int head = g * G + r % G;
-    limit[rt] = ctx_before + pos;  // row sees keys 0 .. limit
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (pos < T) raw = load16(q + (static_cast<int64_t>(pos) * H_q + head) * D + ks * 32 + lg * 8);
-      qb[rt][ks] = __builtin_bit_cast(vec, raw);
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (pos < T) raw = load16(q + (static_cast<int64_t>(pos) * H_q + g * G + r % G) * D + ks * 32 + lg * 8);
+    qb[ks] = __builtin_bit_cast(vec, raw);
   }
 
-  float m[RT], lsum[RT];
-  floatx4_t o[RT][DT];
+  float m = -INFINITY, lsum = 0.0f;
+  floatx4_t o[DT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m[rt] = -INFINITY;
-    lsum[rt] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[rt][dt] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
+  for (int dt = 0; dt < DT; ++dt) o[dt] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const char* kbase = pool_k + layer_off + static_cast<int64_t>(g) * head_stride;
   const char* vbase = pool_v + layer_off + static_cast<int64_t>(g) * head_stride;
 
-  // Staging: K chunks (key, 16-byte dim chunk) and V units (4 keys, 16-byte dim chunk).
-  constexpr int KCH = KT * DCH / kPrefillThreads;                         // K chunks per thread
-  constexpr int VUNITS = (KT / 4) * DCH;                                  // V units per step
-  constexpr int VPT = (VUNITS + kPrefillThreads - 1) / kPrefillThreads;  // V units per thread
-  uint4 kst[KCH];
-  uint4 vst[VPT][4];
+  // The workgroup's slice of the block table, staged once.
+  const int nblk_used = (kmax + BS - 1) / BS;
+  for (int i = tid; i < nblk_used; i += kPrefillThreads) s_table[i] = table[i];
+  __syncthreads();
 
-  auto key_addr = [&](const char* base, int key, int dchunk) -> const char* {
-    const int64_t phys = s_table[key / BS];
-    return base + (phys * BS + key % BS) * static_cast<int64_t>(D * 2) + dchunk * 16;
-  };
-  // Gathers stop at kmax: no row of this workgroup sees a later key (those
-  // tiles are zero-filled), and s_table holds exactly the entries below it.
+  // Staging: thread handles chunk c = tid + i * threads of each tile, i.e.
+  // (key c / DCH, chunk c % DCH); consecutive threads read consecutive 16 B
+  // of one K/V row.  Keys at or past kmax are zero-filled.
+  uint4 kst[CPT], vst[CPT];
   auto gload = [&](int step) {
-    const int key0 = step * KT;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * kPrefillThreads;
-      const int key = key0 + c / DCH;
-      kst[i] = key < kmax ? load16(key_addr(kbase, key, c % DCH)) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + i * kPrefillThreads;
-      if (u < VUNITS) {
-        const int keyq = key0 + (u / DCH) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vst[i][j] = keyq + j < kmax ? load16(key_addr(vbase, keyq + j, u % DCH)) : make_uint4(0, 0, 0, 0);
+      const int key = step * KT + c / DCH;
+      if (key < kmax) {
+        const int64_t phys = s_table[key / BS];
+        const int64_t off = (phys * BS + key % BS) * static_cast<int64_t>(ROWB) + (c % DCH) * 16;
+        kst[i] = load16(kbase + off);
+        vst[i] = load16(vbase + off);
+      } else {
+        kst[i] = make_uint4(0, 0, 0, 0);
+        vst[i] = make_uint4(0, 0, 0, 0);
       }
     }
   };
   auto lds_store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * kPrefillThreads;
-      *reinterpret_cast<uint4*>(&lds_k[buf][(c / DCH) * KROW + (c % DCH) * 16]) = kst[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int u = tid + i * kPrefillThreads;
-      if (u < VUNITS) {
-        const int kq = (u / DCH) * 4;  // first of 4 keys, relative to the step
-        const int local = kq & 31;
-        const int pos = (kq & ~31) + ((local & 15) >> 2) * 8 + (local >> 4) * 4;
-        const uint32_t w[4][4] = {{vst[i][0].x, vst[i][0].y, vst[i][0].z, vst[i][0].w},
-                                  {vst[i][1].x, vst[i][1].y, vst[i][1].z, vst[i][1].w},
-                                  {vst[i][2].x, vst[i][2].y, vst[i][2].z, vst[i][2].w},
-                                  {vst[i][3].x, vst[i][3].y, vst[i][3].z, vst[i][3].w}};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sh = (e & 1) * 16;
-          const uint32_t a0 = (w[0][e >> 1] >> sh) & 0xFFFFu, a1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
-          const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xFFFFu, a3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
-          uint2 pk = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-          const int dim = (u % DCH) * 8 + e;
-          *reinterpret_cast<uint2*>(&lds_v[buf][dim * VROW + vt_col(dim, pos * 2)]) = pk;
-        }
-      }
+      const int kr = c / DCH;
+      const int at = kr * ROWB + swz<DCH>(kr, c % DCH) * 16;
+      *reinterpret_cast<uint4*>(&lds_k[buf][at]) = kst[i];
+      *reinterpret_cast<uint4*>(&lds_v[buf][at]) = vst[i];
     }
   };
-
-  // The workgroup's slice of the block table, staged once: the per-step
-  // gathers then find physical blocks in LDS instead of waiting on a global
-  // load before every K/V load.
-  const int nblk_used = (kmax + BS - 1) / BS;
-  for (int i = tid; i < nblk_used; i += kPrefillThreads) s_table[i] = table[i];
-  __syncthreads();
 
   gload(0);
   lds_store(0);
@@ -206,75 +188,82 @@ __global__ void __launch_bounds__(kPrefillThreads)
     if (step + 1 < nsteps) gload(step + 1);
     const int key0 = step * KT;
 
-    // S^T tiles: 4 key tiles of 16 x RT row tiles.
-    floatx4_t st[RT][KT / 16];
+    // S^T = K Q^T: NT tiles of 16 keys x this wave's 16 rows.
+    floatx4_t st[NT];
 #pragma unroll
-    for (int n = 0; n < KT / 16; ++n) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) st[rt][n] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int n = 0; n < NT; ++n) {
+      st[n] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const int kr = n * 16 + li;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const vec a = *reinterpret_cast<const vec*>(&lds_k[buf][(n * 16 + li) * KROW + (ks * 32 + lg * 8) * 2]);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) st[rt][n] = M::mma(a, qb[rt][ks], st[rt][n]);
+        const vec a = *reinterpret_cast<const vec*>(&lds_k[buf][kr * ROWB + swz<DCH>(kr, ks * 4 + lg) * 16]);
+        st[n] = M::mma(a, qb[ks], st[n]);
       }
     }
 
+    // Online softmax on unscaled scores (for scale > 0 the max commutes with
+    // the scale, which is folded into the exponent).
+    if (scale_log2 <= 0.0f) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) st[n] *= scale_log2;
+    }
+    const float c = scale_log2 > 0.0f ? scale_log2 : 1.0f;
     const bool masked = key0 + KT > first_masked_key;
-    vec pb[RT][KT / 32];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float mx = m[rt];
+    for (int n = 0; n < NT; ++n) {
 #pragma unroll
-      for (int n = 0; n < KT / 16; ++n) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s = st[rt][n][i] * scale_log2;
-          if (masked && key0 + n * 16 + lg * 4 + i > limit[rt]) s = -INFINITY;
-          st[rt][n][i] = s;
-          mx = fmaxf(mx, s);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float ms = (mx == -INFINITY) ? 0.0f : mx;
-      const float alpha = __builtin_amdgcn_exp2f(m[rt] - ms);
-      m[rt] = mx;
-      lsum[rt] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
-#pragma unroll
-      for (int n = 0; n < KT / 16; ++n) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(st[rt][n][i] - ms);
-          lsum[rt] += p;
-          st[rt][n][i] = p;
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KT / 32; ++kk) {
-        uint16_t h[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h[i] = M::cvt(st[rt][2 * kk][i]);
-          h[4 + i] = M::cvt(st[rt][2 * kk + 1][i]);
-        }
-        uint4 raw = make_uint4(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16),
-                               h[4] | (uint32_t(h[5]) << 16), h[6] | (uint32_t(h[7]) << 16));
-        pb[rt][kk] = __builtin_bit_cast(vec, raw);
+      for (int i = 0; i < 4; ++i) {
+        float sv = st[n][i];
+        if (masked && key0 + n * 16 + lg * 4 + i > limit) sv = -INFINITY;
+        st[n][i] = sv;
+        mx = fmaxf(mx, sv);
       }
     }
-
-    // O^T += V^T P^T
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx * c);
+    if (__any(mnew > m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - ((mnew == -INFINITY) ? 0.0f : mnew));
+      m = mnew;
+      lsum *= alpha;
 #pragma unroll
-    for (int kk = 0; kk < KT / 32; ++kk) {
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    const float ms = (m == -INFINITY) ? 0.0f : m;
+    vec pb[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint16_t h[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(st[2 * kk][i], c, -ms));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(st[2 * kk + 1][i], c, -ms));
+        lsum += p0 + p1;
+        h[i] = M::cvt(p0);
+        h[4 + i] = M::cvt(p1);
+      }
+      uint4 raw = make_uint4(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16),
+                             h[4] | (uint32_t(h[5]) << 16), h[6] | (uint32_t(h[7]) << 16));
+      pb[kk] = __builtin_bit_cast(vec, raw);
+    }
+
+    // O^T += V^T P^T.  The lane's P^T operand holds keys kk*32 + lg*4 + [0,4)
+    // then kk*32 + 16 + lg*4 + [0,4) of its row; two transposing reads give
+    // V^T for the same keys at dim dt*16 + li (lane 4k+q addresses key k,
+    // dims 4q..4q+3 of the tile).
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int dim = dt * 16 + li;
-        const vec a = *reinterpret_cast<const vec*>(&lds_v[buf][dim * VROW + vt_col(dim, (kk * 32 + lg * 8) * 2)]);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) o[rt][dt] = M::mma(a, pb[rt][kk], o[rt][dt]);
+        const int k4 = li >> 2, q4 = li & 3;
+        const int dch = dt * 2 + (q4 >> 1), dsub = (q4 & 1) * 8;
+        const int ka = kk * 32 + lg * 4 + k4;
+        const int kb = ka + 16;
+        const uint2 lo = lds_read_tr(&lds_v[buf][ka * ROWB + swz<DCH>(ka, dch) * 16 + dsub]);
+        const uint2 hi = lds_read_tr(&lds_v[buf][kb * ROWB + swz<DCH>(kb, dch) * 16 + dsub]);
+        const vec a = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[dt] = M::mma(a, pb[kk], o[dt]);
       }
     }
 
@@ -282,24 +271,18 @@ __global__ void __launch_bounds__(kPrefillThreads)
     __syncthreads();
   }
 
-  // Normalise and write: lane holds dims dt*16 + lg*4 + [0,4) of row li.
+  // Normalise and write: the lane holds dims dt*16 + lg*4 + [0,4) of row li.
+  float lt = lsum;
+  lt += __shfl_xor(lt, 16);
+  lt += __shfl_xor(lt, 32);
+  if (pos >= T) return;
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  uint16_t* orow = out + (static_cast<int64_t>(pos) * H_q + g * G + r % G) * D;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    float lt = lsum[rt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    const int r = wave * 32 + rt * 16 + li;
-    const int pos = t0 + r / G;
-    if (pos >= T) continue;
-    const int head = g * G + r % G;
-    uint16_t* orow = out + (static_cast<int64_t>(pos) * H_q + head) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint32_t lo = M::cvt(o[rt][dt][0] * inv) | (uint32_t(M::cvt(o[rt][dt][1] * inv)) << 16);
-      const uint32_t hi = M::cvt(o[rt][dt][2] * inv) | (uint32_t(M::cvt(o[rt][dt][3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(orow + dt * 16 + lg * 4) = make_uint2(lo, hi);
-    }
+  for (int dt = 0; dt < DT; ++dt) {
+    const uint32_t lo = M::cvt(o[dt][0] * inv) | (uint32_t(M::cvt(o[dt][1] * inv)) << 16);
+    const uint32_t hi = M::cvt(o[dt][2] * inv) | (uint32_t(M::cvt(o[dt][3] * inv)) << 16);
+    *reinterpret_cast<uint2*>(orow + dt * 16 + lg * 4) = make_uint2(lo, hi);
   }
 }
 
@@ -309,7 +292,7 @@ using PrefillFn = void (*)(const pa_kv_pool*, int32_t, void*, const void*, int32
 template <typename E, int D, int G, int BS>
 static void launch_prefill(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t T, int32_t H_q,
                            const int32_t* table, int32_t ctx_before, float scale_log2, hipStream_t stream) {
-  constexpr int TP = 128 / G;
+  constexpr int TP = 16 * kPrefillWaves / G;
   const int64_t head_stride = static_cast<int64_t>(pool->num_blocks) * BS * D * 2;
   const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * head_stride;
   dim3 grid(static_cast<uint32_t>((T + TP - 1) / TP), pool->num_kv_heads);
