@@ -85,6 +85,17 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Workgroup ids are handed round-robin to the 8 XCDs, each with its own L2.
+// Map id L to work item w so that every XCD gets a contiguous run of work:
+// the workgroups of one KV head then share one L2 for that head's K/V.
+__device__ __forceinline__ int xcd_contiguous(int L, int total) {
+  constexpr int kXcds = 8;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int full = total - (per - 1) * kXcds;  // XCDs that take `per` items; the rest take per - 1
+  const int xcd = L % kXcds, local = L / kXcds;
+  return xcd < full ? xcd * per + local : full * per + (xcd - full) * (per - 1) + local;
+}
+
 template <typename E, int D, int G, int BS>
 __global__ void __launch_bounds__(kPrefillThreads)
     prefill_chunk_kernel(const char* __restrict__ pool_k, const char* __restrict__ pool_v, int64_t layer_off,
@@ -111,8 +122,12 @@ __global__ void __launch_bounds__(kPrefillThreads)
   __shared__ __attribute__((aligned(16))) char lds_v[2][KT * ROWB];
   extern __shared__ int32_t s_table[];  // [ceil(keys needed / BS)]
 
-  const int g = blockIdx.y;
-  const int t0 = blockIdx.x * TP;
+  // Work item w = (KV head, position tile); tiles of a head run last-first,
+  // since later positions see more keys.
+  const int ntiles = (T + TP - 1) / TP;
+  const int w = xcd_contiguous(blockIdx.x, gridDim.x);  // gridDim.x = ntiles * H_kv
+  const int g = w / ntiles;
+  const int t0 = (ntiles - 1 - w % ntiles) * TP;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -295,7 +310,7 @@ static void launch_prefill(const pa_kv_pool* pool, int32_t layer, void* out, con
   constexpr int TP = 16 * kPrefillWaves / G;
   const int64_t head_stride = static_cast<int64_t>(pool->num_blocks) * BS * D * 2;
   const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * head_stride;
-  dim3 grid(static_cast<uint32_t>((T + TP - 1) / TP), pool->num_kv_heads);
+  dim3 grid(static_cast<uint32_t>((T + TP - 1) / TP) * pool->num_kv_heads);
   const size_t table_lds = static_cast<size_t>((static_cast<int64_t>(ctx_before) + T + BS - 1) / BS) * sizeof(int32_t);
   hipLaunchKernelGGL((prefill_chunk_kernel<E, D, G, BS>), grid, dim3(kPrefillThreads), table_lds, stream,
                      static_cast<const char*>(pool->k), static_cast<const char*>(pool->v), layer_off, head_stride,
@@ -348,7 +363,7 @@ extern "C" int pa_prefill_chunk(const pa_kv_pool* pool, int32_t layer, void* out
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(pool->k) |
        reinterpret_cast<uintptr_t>(pool->v)) & 15u)
     return fail(PA_EINVAL, "pa_prefill_chunk: q, out and pool must be 16-byte aligned");
-  if (pool->num_kv_heads > 65535) return fail(PA_EINVAL, "pa_prefill_chunk: grid too large");
+  if (ceil_div(T, 16) * pool->num_kv_heads > INT32_MAX) return fail(PA_EINVAL, "pa_prefill_chunk: grid too large");
   // The kernel keeps its slice of the block table in LDS next to ~70 KB of K/V tiles.
   if (ceil_div(total, pool->block_size) * 4 > 64 * 1024)
     return fail(PA_ENOTSUP, "pa_prefill_chunk: ctx_before + T needs more than 16,384 table entries");
