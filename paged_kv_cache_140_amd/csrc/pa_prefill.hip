@@ -9,24 +9,27 @@
 // are gathered through the sequence's block table ("Block Table 如何工作").
 //
 // How: QK^T and PV are dense contractions, so they run on bf16/f16 MFMA
-// (v_mfma_f32_16x16x32_{bf16,f16}) with fp32 accumulation.
-//  * workgroup = 8 waves x 16 query rows of one KV head: TP = 128/G
+// (v_mfma_f32_32x32x16_{bf16,f16}) with fp32 accumulation.
+//  * workgroup = 4 waves x 32 query rows of one KV head: TP = 128/G
 //    positions x the G query heads that share the KV head, so every K/V tile
 //    staged in LDS serves all G heads.  Row r is (position r / G, head r % G).
-//    16 rows per wave keep the kernel near 160 VGPRs, so several workgroups
-//    share a CU and hide each other's LDS and exp latency.
-//  * keys advance 64 at a time.  The tile is gathered through the table
-//    (staged once in LDS) into double-buffered LDS, K and V both row-major
+//    32 rows per wave make each K/V byte read from LDS feed 32 rows; at 256
+//    registers and 64 KiB of LDS two workgroups share a CU, and their
+//    independent barriers let one's softmax overlap the other's MFMA.
+//  * keys advance 64 at a time.  Each step's K and V tiles go from HBM
+//    straight into double-buffered LDS (global_load_lds_dwordx4), row-major
 //    with an XOR swizzle of the 16-byte chunks that keeps MFMA operand reads
-//    and transposing reads free of bank conflicts beyond 2-way.
+//    and transposing reads free of bank conflicts.  The block id of every
+//    1 KiB load is wave-uniform and read with a scalar load.
 //  * S^T = K Q^T is computed (keys on the MFMA row axis), so the fp32 result
-//    a lane holds -- 4 keys of one query row per 16x16 tile -- is, after the
+//    a lane holds -- 16 keys of one query row per 32x32 tile -- is, after the
 //    softmax, exactly its B operand of O^T += V^T P^T: P never leaves
 //    registers.  The V^T operand comes from two ds_read_b64_tr_b16 reads.
 //  * online softmax in the log2 domain with the scale folded into the
 //    exponent; the running output is rescaled only when a row's maximum
 //    grows, and the causal mask is applied only in the last steps, whose keys
 //    can pass a row's position.
+//  * the output is transposed through LDS and written as whole rows.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -37,42 +40,41 @@ namespace pa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
+// v_mfma_f32_32x32x16_{bf16,f16}.  Lane l supplies A row l%32 and B column
+// l%32 at k = (l/32)*8 + [0,8); it receives D column l%32, rows
+// 8*(v/4) + (l/32)*4 + v%4 for v = 0..15.
 template <typename E>
 struct Mfma;
 template <>
 struct Mfma<BF16> {
   using vec = bf16x8_t;
-  __device__ static floatx4_t mma(vec a, vec b, floatx4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  __device__ static floatx16_t mma(vec a, vec b, floatx16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static uint16_t cvt(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
 };
 template <>
 struct Mfma<F16> {
   using vec = f16x8_t;
-  __device__ static floatx4_t mma(vec a, vec b, floatx4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  __device__ static floatx16_t mma(vec a, vec b, floatx16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
   __device__ static uint16_t cvt(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
 };
 
-constexpr int kPrefillWaves = 8;
+constexpr int kPrefillWaves = 4;
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
+constexpr int kRowsPerWave = 32;
 constexpr int kKeysPerStep = 64;
 
-// 16-byte chunk position of (key, chunk) inside a K or V tile row in LDS.
-// Rows are stored unpadded; the XOR keeps the 16 rows one MFMA operand read
-// touches -- and the 4 rows x 2 chunks one transposing read touches -- on
-// distinct bank groups.
-template <int DCH>
-__device__ __forceinline__ int swz(int key, int chunk) {
-  if constexpr (DCH >= 16)
-    return chunk ^ ((2 * (key & 7) + ((key >> 3) & 1)) & (DCH - 1));
-  else
-    return chunk ^ ((key >> 1) & (DCH - 1));
-}
+// K and V tiles sit in LDS row-major (one key per row, unpadded); the 16-byte
+// chunk c of row `row` is stored at chunk position c ^ swz(row).  The XOR
+// gives 8 consecutive rows 8 distinct bank groups (an MFMA operand read walks
+// 8 rows per LDS cycle) and keeps the chunk pairs {2i, 2i+1} of 4 consecutive
+// rows disjoint (a transposing read covers 32 bytes of each of 4 rows).
+__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
@@ -84,6 +86,25 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
       __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p));
   return __builtin_bit_cast(uint2, v);
 }
+
+// Max / sum of a lane's value and the value of lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l's bytes land at lds + 16*l; lds must be wave-uniform.
+__device__ __forceinline__ void load_to_lds(const char* src, char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void wait_loads_to_lds() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup ids are handed round-robin to the 8 XCDs, each with its own L2.
 // Map id L to work item w so that every XCD gets a contiguous run of work:
@@ -104,23 +125,24 @@ __global__ void __launch_bounds__(kPrefillThreads)
                          float scale_log2) {
   using M = Mfma<E>;
   using vec = typename M::vec;
-  constexpr int ROWS = 16 * kPrefillWaves;  // query rows per workgroup, 16 per wave
-  constexpr int TP = ROWS / G;              // positions per workgroup
-  constexpr int KT = kKeysPerStep;          // keys per step
-  constexpr int KS = D / 32;                // MFMA k-steps over the head dim
-  constexpr int DT = D / 16;                // 16-dim output tiles
-  constexpr int NT = KT / 16;               // 16-key score tiles per step
-  constexpr int KK = KT / 32;               // 32-key PV k-steps per step
-  constexpr int ROWB = D * 2;               // bytes per K/V row in LDS
-  constexpr int DCH = D / 8;                // 16-byte chunks per row
-  constexpr int CPT = KT * DCH / kPrefillThreads;  // chunks per thread per side per step
+  constexpr int ROWS = kRowsPerWave * kPrefillWaves;  // query rows per workgroup
+  constexpr int TP = ROWS / G;                        // positions per workgroup
+  constexpr int KT = kKeysPerStep;                    // keys per step
+  constexpr int KS = D / 16;                          // QK k-steps over the head dim
+  constexpr int DT = D / 32;                          // 32-dim output tiles
+  constexpr int NT = KT / 32;                         // 32-key score tiles per step
+  constexpr int ROWB = D * 2;                         // bytes per K/V row
+  constexpr int DCH = D / 8;                          // 16-byte chunks per row
+  constexpr int TILE = KT * ROWB;                     // bytes of one K or V tile
+  constexpr int RPL = 1024 / ROWB;                    // rows per 1 KiB direct load
+  constexpr int LPW = TILE / 1024 / kPrefillWaves;    // direct loads per wave per side per step
+  constexpr int OSTR = ROWB + 16;                     // row stride of the output staging
   static_assert(ROWS % G == 0, "query group must divide the workgroup's rows");
-  static_assert(KT % BS == 0 || BS % KT == 0, "steps align with blocks");
-  static_assert(CPT >= 1 && KT * DCH % kPrefillThreads == 0, "staging covers the tile");
+  static_assert(BS % RPL == 0, "the rows of one direct load lie in one block");
+  static_assert(LPW >= 1 && TILE % (1024 * kPrefillWaves) == 0, "direct loads cover the tile");
+  static_assert(kPrefillWaves * kRowsPerWave * OSTR <= 2 * 2 * TILE, "output staging fits in the tiles");
 
-  __shared__ __attribute__((aligned(16))) char lds_k[2][KT * ROWB];
-  __shared__ __attribute__((aligned(16))) char lds_v[2][KT * ROWB];
-  extern __shared__ int32_t s_table[];  // [ceil(keys needed / BS)]
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [buffer][K, V]
 
   // Work item w = (KV head, position tile); tiles of a head run last-first,
   // since later positions see more keys.
@@ -128,90 +150,81 @@ __global__ void __launch_bounds__(kPrefillThreads)
   const int w = xcd_contiguous(blockIdx.x, gridDim.x);  // gridDim.x = ntiles * H_kv
   const int g = w / ntiles;
   const int t0 = (ntiles - 1 - w % ntiles) * TP;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int li = lane & 15;
-  const int lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 31;
+  const int h = lane >> 5;
   const int t_last = min(t0 + TP, T) - 1;
   const int kmax = ctx_before + t_last + 1;  // no row of this workgroup sees key kmax or later
   const int nsteps = (kmax + KT - 1) / KT;
   const int first_masked_key = ctx_before + t0 + 1;
 
-  // This lane's query row (MFMA B operand) and its last visible key.
-  vec qb[KS];
-  const int r = wave * 16 + li;
+  // This lane's query row (MFMA B operand: dims ks*16 + h*8 + [0,8)) and its
+  // last visible key.
+  const int r = wave * kRowsPerWave + li;
   const int pos = t0 + r / G;
   const int limit = ctx_before + pos;
+  vec qb[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     uint4 raw = make_uint4(0, 0, 0, 0);
-    if (pos < T) raw = load16(q + (static_cast<int64_t>(pos) * H_q + g * G + r % G) * D + ks * 32 + lg * 8);
+    if (pos < T) raw = load16(q + (static_cast<int64_t>(pos) * H_q + g * G + r % G) * D + ks * 16 + h * 8);
     qb[ks] = __builtin_bit_cast(vec, raw);
   }
-
-  float m = -INFINITY, lsum = 0.0f;
-  floatx4_t o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const char* kbase = pool_k + layer_off + static_cast<int64_t>(g) * head_stride;
   const char* vbase = pool_v + layer_off + static_cast<int64_t>(g) * head_stride;
 
-  // The workgroup's slice of the block table, staged once.
-  const int nblk_used = (kmax + BS - 1) / BS;
-  for (int i = tid; i < nblk_used; i += kPrefillThreads) s_table[i] = table[i];
-  __syncthreads();
-
-  // Staging: thread handles chunk c = tid + i * threads of each tile, i.e.
-  // (key c / DCH, chunk c % DCH); consecutive threads read consecutive 16 B
-  // of one K/V row.  Keys at or past kmax are zero-filled.
-  uint4 kst[CPT], vst[CPT];
-  auto gload = [&](int step) {
+  // Direct global -> LDS loads of one step's K and V tiles.  Load i of this
+  // wave fills 1 KiB of LDS, rows row0 .. row0 + RPL - 1, lane l landing at
+  // byte 16*l: it fetches logical chunk (l % DCH) ^ swz(row).  Keys at or past
+  // kmax are clamped to kmax - 1 (finite data that every row masks out).
+  auto issue = [&](int step, int buf) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * kPrefillThreads;
-      const int key = step * KT + c / DCH;
-      if (key < kmax) {
-        const int64_t phys = s_table[key / BS];
-        const int64_t off = (phys * BS + key % BS) * static_cast<int64_t>(ROWB) + (c % DCH) * 16;
-        kst[i] = load16(kbase + off);
-        vst[i] = load16(vbase + off);
-      } else {
-        kst[i] = make_uint4(0, 0, 0, 0);
-        vst[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto lds_store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * kPrefillThreads;
-      const int kr = c / DCH;
-      const int at = kr * ROWB + swz<DCH>(kr, c % DCH) * 16;
-      *reinterpret_cast<uint4*>(&lds_k[buf][at]) = kst[i];
-      *reinterpret_cast<uint4*>(&lds_v[buf][at]) = vst[i];
+    for (int i = 0; i < LPW; ++i) {
+      const int row0 = (wave * LPW + i) * RPL;
+      const int row = row0 + lane / DCH;
+      const int bkey = min(step * KT + row0, kmax - 1);  // wave-uniform; same block as every clamped key
+      const int key = min(step * KT + row, kmax - 1);
+      const int64_t blk = table[bkey / BS];
+      const int64_t off = (blk * BS + (key & (BS - 1))) * ROWB + (((lane % DCH) ^ swz(row)) * 16);
+      load_to_lds(kbase + off, &lds[buf][0][(wave * LPW + i) * 1024]);
+      load_to_lds(vbase + off, &lds[buf][1][(wave * LPW + i) * 1024]);
     }
   };
 
-  gload(0);
-  lds_store(0);
+  float m = -INFINITY, lsum = 0.0f;
+  floatx16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = floatx16_t{};
+
+  // Transposing-read geometry: this lane, as source lane 4*k4 + q4 of its
+  // 16-lane group g16, addresses row 4*(g16/2) + k4 (+8) of a 16-key slice,
+  // dims dt*32 + (g16%2)*16 + 4*q4 + [0,4).
+  const int g16 = lane >> 4, k4 = (lane >> 2) & 3, q4 = lane & 3;
+  const int vrow = 4 * (g16 >> 1) + k4;
+  const int vsw = swz(vrow);  // swz(vrow + 8 + 16 s + 32 n) is the same
+
+  issue(0, 0);
+  wait_loads_to_lds();
   __syncthreads();
 
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
-    if (step + 1 < nsteps) gload(step + 1);
+    if (step + 1 < nsteps) issue(step + 1, buf ^ 1);
+    const char* kt = lds[buf][0];
+    const char* vt = lds[buf][1];
     const int key0 = step * KT;
 
-    // S^T = K Q^T: NT tiles of 16 keys x this wave's 16 rows.
-    floatx4_t st[NT];
+    // S^T = K Q^T: NT tiles of 32 keys x this wave's 32 rows.  The lane holds
+    // keys n*32 + 8*(v/4) + 4*h + v%4 of row li.
+    floatx16_t st[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      st[n] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      const int kr = n * 16 + li;
+      st[n] = floatx16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const vec a = *reinterpret_cast<const vec*>(&lds_k[buf][kr * ROWB + swz<DCH>(kr, ks * 4 + lg) * 16]);
+        const vec a = *reinterpret_cast<const vec*>(kt + (n * 32 + li) * ROWB + (((ks * 2 + h) ^ swz(li)) * 16));
         st[n] = M::mma(a, qb[ks], st[n]);
       }
     }
@@ -228,15 +241,14 @@ __global__ void __launch_bounds__(kPrefillThreads)
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sv = st[n][i];
-        if (masked && key0 + n * 16 + lg * 4 + i > limit) sv = -INFINITY;
-        st[n][i] = sv;
+      for (int v = 0; v < 16; ++v) {
+        float sv = st[n][v];
+        if (masked && key0 + n * 32 + 8 * (v >> 2) + 4 * h + (v & 3) > limit) sv = -INFINITY;
+        st[n][v] = sv;
         mx = fmaxf(mx, sv);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     const float mnew = fmaxf(m, mx * c);
     if (__any(mnew > m)) {
       const float alpha = __builtin_amdgcn_exp2f(m - ((mnew == -INFINITY) ? 0.0f : mnew));
@@ -246,58 +258,77 @@ __global__ void __launch_bounds__(kPrefillThreads)
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     }
     const float ms = (m == -INFINITY) ? 0.0f : m;
-    vec pb[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      uint16_t h[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(st[2 * kk][i], c, -ms));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(st[2 * kk + 1][i], c, -ms));
-        lsum += p0 + p1;
-        h[i] = M::cvt(p0);
-        h[4 + i] = M::cvt(p1);
-      }
-      uint4 raw = make_uint4(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16),
-                             h[4] | (uint32_t(h[5]) << 16), h[6] | (uint32_t(h[7]) << 16));
-      pb[kk] = __builtin_bit_cast(vec, raw);
-    }
 
-    // O^T += V^T P^T.  The lane's P^T operand holds keys kk*32 + lg*4 + [0,4)
-    // then kk*32 + 16 + lg*4 + [0,4) of its row; two transposing reads give
-    // V^T for the same keys at dim dt*16 + li (lane 4k+q addresses key k,
-    // dims 4q..4q+3 of the tile).
+    // P^T operand for 16-key slice (n, s): slots 0..7 of this lane are keys
+    // n*32 + 16s + 4h + [0,4) and n*32 + 16s + 8 + 4h + [0,4), i.e. its score
+    // values 8s .. 8s+7 of tile n.
+    vec pb[NT][2];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int n = 0; n < NT; ++n) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int k4 = li >> 2, q4 = li & 3;
-        const int dch = dt * 2 + (q4 >> 1), dsub = (q4 & 1) * 8;
-        const int ka = kk * 32 + lg * 4 + k4;
-        const int kb = ka + 16;
-        const uint2 lo = lds_read_tr(&lds_v[buf][ka * ROWB + swz<DCH>(ka, dch) * 16 + dsub]);
-        const uint2 hi = lds_read_tr(&lds_v[buf][kb * ROWB + swz<DCH>(kb, dch) * 16 + dsub]);
-        const vec a = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[dt] = M::mma(a, pb[kk], o[dt]);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        uint16_t hh[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(st[n][8 * s2 + i], c, -ms));
+          lsum += p;
+          hh[i] = M::cvt(p);
+        }
+        const uint4 raw = make_uint4(hh[0] | (uint32_t(hh[1]) << 16), hh[2] | (uint32_t(hh[3]) << 16),
+                                     hh[4] | (uint32_t(hh[5]) << 16), hh[6] | (uint32_t(hh[7]) << 16));
+        pb[n][s2] = __builtin_bit_cast(vec, raw);
       }
     }
 
-    if (step + 1 < nsteps) lds_store(buf ^ 1);
+    // O^T += V^T P^T.  The V^T operand for dims dt*32 + li and the same 8 keys
+    // comes from two transposing reads (rows vrow and vrow + 8 of the slice).
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int rw = n * 32 + s2 * 16 + vrow;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int ch = (dt * 4 + (g16 & 1) * 2 + (q4 >> 1)) ^ vsw;
+          const uint2 lo = lds_read_tr(vt + rw * ROWB + ch * 16 + (q4 & 1) * 8);
+          const uint2 hi = lds_read_tr(vt + (rw + 8) * ROWB + ch * 16 + (q4 & 1) * 8);
+          const vec a = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          o[dt] = M::mma(a, pb[n][s2], o[dt]);
+        }
+      }
+    }
+
+    wait_loads_to_lds();
     __syncthreads();
   }
 
-  // Normalise and write: the lane holds dims dt*16 + lg*4 + [0,4) of row li.
-  float lt = lsum;
-  lt += __shfl_xor(lt, 16);
-  lt += __shfl_xor(lt, 32);
-  if (pos >= T) return;
+  // Normalise; stage the wave's 32 x D output rows in LDS (the tiles are no
+  // longer read) and write whole rows.  The lane holds dims
+  // dt*32 + 8*j + 4*h + [0,4) of row li, j = 0..3.
+  const float lt = sum_halves(lsum);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  uint16_t* orow = out + (static_cast<int64_t>(pos) * H_q + g * G + r % G) * D;
+  char* ob = &lds[0][0][0] + wave * kRowsPerWave * OSTR;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    const uint32_t lo = M::cvt(o[dt][0] * inv) | (uint32_t(M::cvt(o[dt][1] * inv)) << 16);
-    const uint32_t hi = M::cvt(o[dt][2] * inv) | (uint32_t(M::cvt(o[dt][3] * inv)) << 16);
-    *reinterpret_cast<uint2*>(orow + dt * 16 + lg * 4) = make_uint2(lo, hi);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = M::cvt(o[dt][4 * j] * inv) | (uint32_t(M::cvt(o[dt][4 * j + 1] * inv)) << 16);
+      const uint32_t hi = M::cvt(o[dt][4 * j + 2] * inv) | (uint32_t(M::cvt(o[dt][4 * j + 3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(ob + li * OSTR + (dt * 32 + 8 * j + 4 * h) * 2) = make_uint2(lo, hi);
+    }
+  }
+  __syncthreads();
+  constexpr int OCH = kRowsPerWave * DCH / 64;  // 16-byte chunks per lane
+#pragma unroll
+  for (int i = 0; i < OCH; ++i) {
+    const int idx = i * 64 + lane;
+    const int orow = idx / DCH, och = idx % DCH;
+    const int rr = wave * kRowsPerWave + orow;
+    const int opos = t0 + rr / G;
+    if (opos < T) {
+      const uint4 val = *reinterpret_cast<const uint4*>(ob + orow * OSTR + och * 16);
+      *reinterpret_cast<uint4*>(out + (static_cast<int64_t>(opos) * H_q + g * G + rr % G) * D + och * 8) = val;
+    }
   }
 }
 
@@ -307,12 +338,11 @@ using PrefillFn = void (*)(const pa_kv_pool*, int32_t, void*, const void*, int32
 template <typename E, int D, int G, int BS>
 static void launch_prefill(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t T, int32_t H_q,
                            const int32_t* table, int32_t ctx_before, float scale_log2, hipStream_t stream) {
-  constexpr int TP = 16 * kPrefillWaves / G;
+  constexpr int TP = kRowsPerWave * kPrefillWaves / G;
   const int64_t head_stride = static_cast<int64_t>(pool->num_blocks) * BS * D * 2;
   const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * head_stride;
   dim3 grid(static_cast<uint32_t>((T + TP - 1) / TP) * pool->num_kv_heads);
-  const size_t table_lds = static_cast<size_t>((static_cast<int64_t>(ctx_before) + T + BS - 1) / BS) * sizeof(int32_t);
-  hipLaunchKernelGGL((prefill_chunk_kernel<E, D, G, BS>), grid, dim3(kPrefillThreads), table_lds, stream,
+  hipLaunchKernelGGL((prefill_chunk_kernel<E, D, G, BS>), grid, dim3(kPrefillThreads), 0, stream,
                      static_cast<const char*>(pool->k), static_cast<const char*>(pool->v), layer_off, head_stride,
                      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), table, T, H_q, ctx_before,
                      scale_log2);
@@ -364,9 +394,6 @@ extern "C" int pa_prefill_chunk(const pa_kv_pool* pool, int32_t layer, void* out
        reinterpret_cast<uintptr_t>(pool->v)) & 15u)
     return fail(PA_EINVAL, "pa_prefill_chunk: q, out and pool must be 16-byte aligned");
   if (ceil_div(T, 16) * pool->num_kv_heads > INT32_MAX) return fail(PA_EINVAL, "pa_prefill_chunk: grid too large");
-  // The kernel keeps its slice of the block table in LDS next to ~70 KB of K/V tiles.
-  if (ceil_div(total, pool->block_size) * 4 > 64 * 1024)
-    return fail(PA_ENOTSUP, "pa_prefill_chunk: ctx_before + T needs more than 16,384 table entries");
   const int G = H_q / pool->num_kv_heads;
   PrefillFn fn = nullptr;
   if (pool->dtype == PA_BF16) fn = prefill_d<BF16>(pool->head_dim, G, pool->block_size);
