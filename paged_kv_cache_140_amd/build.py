@@ -24,7 +24,11 @@ LIB = os.path.join(PKG, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# -amdgpu-mfma-vgpr-form: MFMA results stay in VGPRs.  Otherwise the prefill
+# kernel's accumulators land in AGPRs and every rescale or softmax read of
+# them costs a v_accvgpr copy (and the kernel exceeds 256 registers).
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def sources():

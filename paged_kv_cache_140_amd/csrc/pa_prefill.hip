@@ -136,13 +136,18 @@ __global__ void __launch_bounds__(kPrefillThreads)
   constexpr int TILE = KT * ROWB;                     // bytes of one K or V tile
   constexpr int RPL = 1024 / ROWB;                    // rows per 1 KiB direct load
   constexpr int LPW = TILE / 1024 / kPrefillWaves;    // direct loads per wave per side per step
-  constexpr int OSTR = ROWB + 16;                     // row stride of the output staging
   static_assert(ROWS % G == 0, "query group must divide the workgroup's rows");
   static_assert(BS % RPL == 0, "the rows of one direct load lie in one block");
   static_assert(LPW >= 1 && TILE % (1024 * kPrefillWaves) == 0, "direct loads cover the tile");
-  static_assert(kPrefillWaves * kRowsPerWave * OSTR <= 2 * 2 * TILE, "output staging fits in the tiles");
+  static_assert(kPrefillWaves == 4 && kRowsPerWave * ROWB <= TILE, "each wave stages its output in one tile array");
 
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [buffer][K, V]
+  // Double-buffered K and V tiles as four distinct arrays: the compiler can
+  // then tell that the next tile's direct loads never alias the tile being
+  // read, and adds no wait for them before the reads.
+  __shared__ __attribute__((aligned(1024))) char lk0[TILE];
+  __shared__ __attribute__((aligned(1024))) char lv0[TILE];
+  __shared__ __attribute__((aligned(1024))) char lk1[TILE];
+  __shared__ __attribute__((aligned(1024))) char lv1[TILE];
 
   // Work item w = (KV head, position tile); tiles of a head run last-first,
   // since later positions see more keys.
@@ -175,21 +180,35 @@ __global__ void __launch_bounds__(kPrefillThreads)
   const char* kbase = pool_k + layer_off + static_cast<int64_t>(g) * head_stride;
   const char* vbase = pool_v + layer_off + static_cast<int64_t>(g) * head_stride;
 
-  // Direct global -> LDS loads of one step's K and V tiles.  Load i of this
-  // wave fills 1 KiB of LDS, rows row0 .. row0 + RPL - 1, lane l landing at
-  // byte 16*l: it fetches logical chunk (l % DCH) ^ swz(row).  Keys at or past
-  // kmax are clamped to kmax - 1 (finite data that every row masks out).
-  auto issue = [&](int step, int buf) {
+  // Direct global -> LDS loads of one step's K and V tiles.  This wave's
+  // loads cover rows wave*WROWS + [0, WROWS) of the tile; load i fills 1 KiB
+  // of LDS, rows row0 .. row0 + RPL - 1, lane l landing at byte 16*l: it
+  // fetches logical chunk (l % DCH) ^ swz(row).  Keys at or past kmax are
+  // clamped to kmax - 1 (finite data that every row masks out).
+  constexpr int WROWS = LPW * RPL;                  // tile rows per wave
+  constexpr int NBW = WROWS >= BS ? WROWS / BS : 1;  // blocks those rows touch
+  struct Blocks {
+    int32_t b[NBW];
+  };
+  // Block ids of this wave's rows at `step` (wave-uniform, scalar loads).
+  // Entry j serves rows from j*BS on; clamping the key first keeps every
+  // clamped row's block.
+  auto fetch = [&](int step) {
+    Blocks bl;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) bl.b[j] = table[min(step * KT + wave * WROWS + j * BS, kmax - 1) / BS];
+    return bl;
+  };
+  auto issue = [&](int step, const Blocks& bl, char* kdst, char* vdst) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int row0 = (wave * LPW + i) * RPL;
+      const int row0 = wave * WROWS + i * RPL;
       const int row = row0 + lane / DCH;
-      const int bkey = min(step * KT + row0, kmax - 1);  // wave-uniform; same block as every clamped key
       const int key = min(step * KT + row, kmax - 1);
-      const int64_t blk = table[bkey / BS];
+      const int64_t blk = bl.b[NBW > 1 ? i * RPL / BS : 0];
       const int64_t off = (blk * BS + (key & (BS - 1))) * ROWB + (((lane % DCH) ^ swz(row)) * 16);
-      load_to_lds(kbase + off, &lds[buf][0][(wave * LPW + i) * 1024]);
-      load_to_lds(vbase + off, &lds[buf][1][(wave * LPW + i) * 1024]);
+      load_to_lds(kbase + off, kdst + row0 * ROWB);
+      load_to_lds(vbase + off, vdst + row0 * ROWB);
     }
   };
 
@@ -205,15 +224,11 @@ __global__ void __launch_bounds__(kPrefillThreads)
   const int vrow = 4 * (g16 >> 1) + k4;
   const int vsw = swz(vrow);  // swz(vrow + 8 + 16 s + 32 n) is the same
 
-  issue(0, 0);
-  wait_loads_to_lds();
-  __syncthreads();
-
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    if (step + 1 < nsteps) issue(step + 1, buf ^ 1);
-    const char* kt = lds[buf][0];
-    const char* vt = lds[buf][1];
+  // One step: attend to the tile in (kt, vt) while the next step's tile
+  // streams into (kn, vn).
+  Blocks next = fetch(0);
+  auto step_body = [&](int step, const char* kt, const char* vt, char* kn, char* vn) {
+    if (step + 1 < nsteps) issue(step + 1, next, kn, vn);
     const int key0 = step * KT;
 
     // S^T = K Q^T: NT tiles of 32 keys x this wave's 32 rows.  The lane holds
@@ -228,6 +243,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
         st[n] = M::mma(a, qb[ks], st[n]);
       }
     }
+    next = fetch(step + 2);
 
     // Online softmax on unscaled scores (for scale > 0 the max commutes with
     // the scale, which is folded into the exponent).
@@ -300,21 +316,33 @@ __global__ void __launch_bounds__(kPrefillThreads)
 
     wait_loads_to_lds();
     __syncthreads();
+  };
+
+  issue(0, next, lk0, lv0);
+  next = fetch(1);
+  wait_loads_to_lds();
+  __syncthreads();
+  for (int step = 0; step < nsteps; step += 2) {
+    step_body(step, lk0, lv0, lk1, lv1);
+    if (step + 1 >= nsteps) break;
+    step_body(step + 1, lk1, lv1, lk0, lv0);
   }
 
-  // Normalise; stage the wave's 32 x D output rows in LDS (the tiles are no
-  // longer read) and write whole rows.  The lane holds dims
-  // dt*32 + 8*j + 4*h + [0,4) of row li, j = 0..3.
+  // Normalise; stage the wave's 32 x D output rows in LDS (wave w takes one
+  // of the four tile arrays, no longer read) and write whole rows.  The lane
+  // holds dims dt*32 + 8*j + 4*h + [0,4) of row li, j = 0..3; chunk c of row
+  // rr is stored at chunk position c ^ (rr % DCH).
   const float lt = sum_halves(lsum);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  char* ob = &lds[0][0][0] + wave * kRowsPerWave * OSTR;
+  char* ob = wave == 0 ? lk0 : wave == 1 ? lv0 : wave == 2 ? lk1 : lv1;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t lo = M::cvt(o[dt][4 * j] * inv) | (uint32_t(M::cvt(o[dt][4 * j + 1] * inv)) << 16);
       const uint32_t hi = M::cvt(o[dt][4 * j + 2] * inv) | (uint32_t(M::cvt(o[dt][4 * j + 3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(ob + li * OSTR + (dt * 32 + 8 * j + 4 * h) * 2) = make_uint2(lo, hi);
+      const int chunk = (dt * 4 + j) ^ (li % DCH);
+      *reinterpret_cast<uint2*>(ob + li * ROWB + chunk * 16 + h * 8) = make_uint2(lo, hi);
     }
   }
   __syncthreads();
@@ -326,7 +354,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
     const int rr = wave * kRowsPerWave + orow;
     const int opos = t0 + rr / G;
     if (opos < T) {
-      const uint4 val = *reinterpret_cast<const uint4*>(ob + orow * OSTR + och * 16);
+      const uint4 val = *reinterpret_cast<const uint4*>(ob + orow * ROWB + ((och ^ (orow % DCH)) * 16));
       *reinterpret_cast<uint4*>(out + (static_cast<int64_t>(opos) * H_q + g * G + rr % G) * D + och * 8) = val;
     }
   }
