@@ -70,11 +70,19 @@ constexpr int kRowsPerWave = 32;
 constexpr int kKeysPerStep = 64;
 
 // K and V tiles sit in LDS row-major (one key per row, unpadded); the 16-byte
-// chunk c of row `row` is stored at chunk position c ^ swz(row).  The XOR
-// gives 8 consecutive rows 8 distinct bank groups (an MFMA operand read walks
-// 8 rows per LDS cycle) and keeps the chunk pairs {2i, 2i+1} of 4 consecutive
-// rows disjoint (a transposing read covers 32 bytes of each of 4 rows).
-__device__ __forceinline__ int swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+// chunk c of row `row` is stored at chunk position c ^ swz(row).  LDS serves
+// a 16-byte read 16 lanes at a time and an 8-byte read 32 lanes at a time,
+// each pass over 256 bytes of banks.  The XOR makes both passes touch 256
+// distinct bytes: the MFMA operand read (16 consecutive rows, one chunk each)
+// and the transposing read (4 consecutive rows, the 4 chunks of one 32-dim
+// slice each).  It depends on row & 15 only.
+template <int DCH>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (DCH >= 16)
+    return 4 * (row & 3) + ((row >> 2) & 3);  // 256-byte rows
+  else
+    return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);  // 128-byte rows: two per 256 bytes
+}
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
@@ -206,7 +214,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
       const int row = row0 + lane / DCH;
       const int key = min(step * KT + row, kmax - 1);
       const int64_t blk = bl.b[NBW > 1 ? i * RPL / BS : 0];
-      const int64_t off = (blk * BS + (key & (BS - 1))) * ROWB + (((lane % DCH) ^ swz(row)) * 16);
+      const int64_t off = (blk * BS + (key & (BS - 1))) * ROWB + (((lane % DCH) ^ swz<DCH>(row)) * 16);
       load_to_lds(kbase + off, kdst + row0 * ROWB);
       load_to_lds(vbase + off, vdst + row0 * ROWB);
     }
@@ -222,7 +230,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
   // dims dt*32 + (g16%2)*16 + 4*q4 + [0,4).
   const int g16 = lane >> 4, k4 = (lane >> 2) & 3, q4 = lane & 3;
   const int vrow = 4 * (g16 >> 1) + k4;
-  const int vsw = swz(vrow);  // swz(vrow + 8 + 16 s + 32 n) is the same
+  const int vsw_lo = swz<DCH>(vrow), vsw_hi = swz<DCH>(vrow + 8);  // the same for + 16 s + 32 n
 
   // One step: attend to the tile in (kt, vt) while the next step's tile
   // streams into (kn, vn).
@@ -239,7 +247,8 @@ __global__ void __launch_bounds__(kPrefillThreads)
       st[n] = floatx16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const vec a = *reinterpret_cast<const vec*>(kt + (n * 32 + li) * ROWB + (((ks * 2 + h) ^ swz(li)) * 16));
+        const vec a =
+            *reinterpret_cast<const vec*>(kt + (n * 32 + li) * ROWB + (((ks * 2 + h) ^ swz<DCH>(li)) * 16));
         st[n] = M::mma(a, qb[ks], st[n]);
       }
     }
@@ -252,18 +261,18 @@ __global__ void __launch_bounds__(kPrefillThreads)
       for (int n = 0; n < NT; ++n) st[n] *= scale_log2;
     }
     const float c = scale_log2 > 0.0f ? scale_log2 : 1.0f;
-    const bool masked = key0 + KT > first_masked_key;
+    if (key0 + KT > first_masked_key) {  // uniform: only the last steps reach past a row's position
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (key0 + n * 32 + 8 * (v >> 2) + 4 * h + (v & 3) > limit) st[n][v] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
+    for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float sv = st[n][v];
-        if (masked && key0 + n * 32 + 8 * (v >> 2) + 4 * h + (v & 3) > limit) sv = -INFINITY;
-        st[n][v] = sv;
-        mx = fmaxf(mx, sv);
-      }
-    }
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[n][v]);
     mx = max_halves(mx);
     const float mnew = fmaxf(m, mx * c);
     if (__any(mnew > m)) {
@@ -305,9 +314,9 @@ __global__ void __launch_bounds__(kPrefillThreads)
         const int rw = n * 32 + s2 * 16 + vrow;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int ch = (dt * 4 + (g16 & 1) * 2 + (q4 >> 1)) ^ vsw;
-          const uint2 lo = lds_read_tr(vt + rw * ROWB + ch * 16 + (q4 & 1) * 8);
-          const uint2 hi = lds_read_tr(vt + (rw + 8) * ROWB + ch * 16 + (q4 & 1) * 8);
+          const int ch = dt * 4 + (g16 & 1) * 2 + (q4 >> 1);
+          const uint2 lo = lds_read_tr(vt + rw * ROWB + (ch ^ vsw_lo) * 16 + (q4 & 1) * 8);
+          const uint2 hi = lds_read_tr(vt + (rw + 8) * ROWB + (ch ^ vsw_hi) * 16 + (q4 & 1) * 8);
           const vec a = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
           o[dt] = M::mma(a, pb[n][s2], o[dt]);
         }
