@@ -10,17 +10,19 @@
 //
 // How: QK^T and PV are dense contractions, so they run on bf16/f16 MFMA
 // (v_mfma_f32_32x32x16_{bf16,f16}) with fp32 accumulation.
-//  * workgroup = 4 waves x 32 query rows of one KV head: TP = 128/G
+//  * workgroup = 8 waves x 32 query rows of one KV head: TP = 256/G
 //    positions x the G query heads that share the KV head, so every K/V tile
 //    staged in LDS serves all G heads.  Row r is (position r / G, head r % G).
-//    32 rows per wave make each K/V byte read from LDS feed 32 rows; at 256
-//    registers and 64 KiB of LDS two workgroups share a CU, and their
-//    independent barriers let one's softmax overlap the other's MFMA.
-//  * keys advance 64 at a time.  Each step's K and V tiles go from HBM
-//    straight into double-buffered LDS (global_load_lds_dwordx4), row-major
-//    with an XOR swizzle of the 16-byte chunks that keeps MFMA operand reads
-//    and transposing reads free of bank conflicts.  The block id of every
-//    1 KiB load is wave-uniform and read with a scalar load.
+//    32 rows per wave make each K/V byte read from LDS feed 32 rows.
+//  * ping-pong: waves 0-3 and 4-7 run the same sequence of MFMA units (QK of
+//    the next step + PV of this one) and softmax units one phase apart, so
+//    on every SIMD one wave keeps the matrix core busy while the other works
+//    on the vector ALU.
+//  * keys advance 64 at a time.  K and V tiles go from HBM straight into
+//    double-buffered LDS (global_load_lds_dwordx4), K one step ahead of V,
+//    in a layout that keeps MFMA operand reads and transposing reads free of
+//    bank conflicts.  The block id of every load is wave-uniform and read
+//    with a scalar load.
 //  * S^T = K Q^T is computed (keys on the MFMA row axis), so the fp32 result
 //    a lane holds -- 16 keys of one query row per 32x32 tile -- is, after the
 //    softmax, exactly its B operand of O^T += V^T P^T: P never leaves
@@ -33,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "pa_common.h"
 
@@ -64,24 +67,23 @@ struct Mfma<F16> {
   __device__ static uint16_t cvt(float x) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x)); }
 };
 
-constexpr int kPrefillWaves = 4;
+constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kKeysPerStep = 64;
 
-// K and V tiles sit in LDS row-major (one key per row, unpadded); the 16-byte
-// chunk c of row `row` is stored at chunk position c ^ swz(row).  LDS serves
-// a 16-byte read 16 lanes at a time and an 8-byte read 32 lanes at a time,
-// each pass over 256 bytes of banks.  The XOR makes both passes touch 256
-// distinct bytes: the MFMA operand read (16 consecutive rows, one chunk each)
-// and the transposing read (4 consecutive rows, the 4 chunks of one 32-dim
-// slice each).  It depends on row & 15 only.
-template <int DCH>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (DCH >= 16)
-    return 4 * (row & 3) + ((row >> 2) & 3);  // 256-byte rows
-  else
-    return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);  // 128-byte rows: two per 256 bytes
+// LDS tile layout for K and V (KT keys x D dims, 16-bit): columns of 64
+// bytes (4 chunks of 16 bytes, 32 dims) are stored one after another, each
+// as KT rows of 64 bytes, and the 4 chunks of row `row` are rotated by
+// (row >> 2) & 3.  LDS serves a 16-byte read 16 lanes at a time and an
+// 8-byte read 32 lanes at a time, each pass over 256 bytes of banks; this
+// layout makes both passes touch 256 distinct bytes for the MFMA operand
+// read (16 consecutive rows, one chunk each) and the transposing read (4
+// consecutive rows, the 4 chunks of one column each), and every lane's
+// address is a per-lane base plus a compile-time offset.
+template <int KT>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return (chunk >> 2) * (KT * 64) + row * 64 + (((chunk & 3) ^ ((row >> 2) & 3)) * 16);
 }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -112,7 +114,24 @@ __device__ __forceinline__ void load_to_lds(const char* src, char* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 #endif
 }
-__device__ __forceinline__ void wait_loads_to_lds() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as a builtin
+// so that the compiler's own wait tracking knows the loads have landed.
+__device__ __forceinline__ void wait_loads_to_lds() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier without a memory fence (a fence would wait for every
+// direct load in flight): this wave's LDS reads are complete (lgkmcnt(0), so
+// no buffer is overwritten under a pending read), the compiler keeps every
+// instruction on its side of it (so the units of the ping-pong stay in their
+// phases), and loads into LDS stay in flight.  Each wave waits for its own
+// loads before the barrier that precedes their first reader.
+__device__ __forceinline__ void barrier_keep_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Workgroup ids are handed round-robin to the 8 XCDs, each with its own L2.
 // Map id L to work item w so that every XCD gets a contiguous run of work:
@@ -142,20 +161,18 @@ __global__ void __launch_bounds__(kPrefillThreads)
   constexpr int ROWB = D * 2;                         // bytes per K/V row
   constexpr int DCH = D / 8;                          // 16-byte chunks per row
   constexpr int TILE = KT * ROWB;                     // bytes of one K or V tile
-  constexpr int RPL = 1024 / ROWB;                    // rows per 1 KiB direct load
-  constexpr int LPW = TILE / 1024 / kPrefillWaves;    // direct loads per wave per side per step
+  constexpr int RG = KT / 16;                         // 16-row groups per tile (one 1 KiB load each per column)
+  constexpr int LPW = TILE / 1024 / kPrefillWaves;    // direct loads per wave per tile
   static_assert(ROWS % G == 0, "query group must divide the workgroup's rows");
-  static_assert(BS % RPL == 0, "the rows of one direct load lie in one block");
-  static_assert(LPW >= 1 && TILE % (1024 * kPrefillWaves) == 0, "direct loads cover the tile");
-  static_assert(kPrefillWaves == 4 && kRowsPerWave * ROWB <= TILE, "each wave stages its output in one tile array");
+  static_assert(LPW >= 1 && TILE % (1024 * kPrefillWaves) == 0 && kPrefillWaves % RG == 0,
+                "direct loads cover the tile, one row group per wave");
+  static_assert(DCH % 4 == 0 && BS >= 8, "whole 64-byte columns; at most two blocks per row group");
+  static_assert(2 * kRowsPerWave * ROWB <= TILE, "two waves stage their output in one tile");
 
-  // Double-buffered K and V tiles as four distinct arrays: the compiler can
-  // then tell that the next tile's direct loads never alias the tile being
-  // read, and adds no wait for them before the reads.
-  __shared__ __attribute__((aligned(1024))) char lk0[TILE];
-  __shared__ __attribute__((aligned(1024))) char lv0[TILE];
-  __shared__ __attribute__((aligned(1024))) char lk1[TILE];
-  __shared__ __attribute__((aligned(1024))) char lv1[TILE];
+  // Double-buffered K and V tiles: lds[0..1] K, lds[2..3] V.  Every access
+  // names its buffer with a compile-time index, so the compiler sees that
+  // direct loads into one buffer never alias reads of another.
+  __shared__ __attribute__((aligned(1024))) char lds[4][TILE];
 
   // Work item w = (KV head, position tile); tiles of a head run last-first,
   // since later positions see more keys.
@@ -171,6 +188,9 @@ __global__ void __launch_bounds__(kPrefillThreads)
   const int kmax = ctx_before + t_last + 1;  // no row of this workgroup sees key kmax or later
   const int nsteps = (kmax + KT - 1) / KT;
   const int first_masked_key = ctx_before + t0 + 1;
+  // Waves 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise and run
+  // the same work one phase apart.
+  const bool group_b = wave >= kPrefillWaves / 2;
 
   // This lane's query row (MFMA B operand: dims ks*16 + h*8 + [0,8)) and its
   // last visible key.
@@ -188,74 +208,126 @@ __global__ void __launch_bounds__(kPrefillThreads)
   const char* kbase = pool_k + layer_off + static_cast<int64_t>(g) * head_stride;
   const char* vbase = pool_v + layer_off + static_cast<int64_t>(g) * head_stride;
 
-  // Direct global -> LDS loads of one step's K and V tiles.  This wave's
-  // loads cover rows wave*WROWS + [0, WROWS) of the tile; load i fills 1 KiB
-  // of LDS, rows row0 .. row0 + RPL - 1, lane l landing at byte 16*l: it
-  // fetches logical chunk (l % DCH) ^ swz(row).  Keys at or past kmax are
-  // clamped to kmax - 1 (finite data that every row masks out).
-  constexpr int WROWS = LPW * RPL;                  // tile rows per wave
-  constexpr int NBW = WROWS >= BS ? WROWS / BS : 1;  // blocks those rows touch
+  // Direct global -> LDS loads of one K or V tile.  This wave loads row
+  // group rg = wave % RG (rows 16*rg + [0,16)) of columns cg0 .. cg0+LPW-1;
+  // each load fills 1 KiB of LDS (16 rows x 64 bytes), lane l landing at
+  // byte 16*l: row 16*rg + l/4, rotated chunk position l % 4.  Keys at or
+  // past kmax are clamped to kmax - 1 (finite data that every row masks out).
+  const int rg = wave % RG, cg0 = (wave / RG) * LPW;
+  const int lrow = rg * 16 + (lane >> 2);                         // tile row this lane loads
+  const int lchunk = ((lane & 3) ^ ((lrow >> 2) & 3)) * 16;       // byte of its chunk within the column
   struct Blocks {
-    int32_t b[NBW];
+    int32_t lo, hi;  // block ids of rows 16*rg + [0,8) and + [8,16) (the same when BS >= 16)
   };
-  // Block ids of this wave's rows at `step` (wave-uniform, scalar loads).
-  // Entry j serves rows from j*BS on; clamping the key first keeps every
-  // clamped row's block.
-  auto fetch = [&](int step) {
-    Blocks bl;
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) bl.b[j] = table[min(step * KT + wave * WROWS + j * BS, kmax - 1) / BS];
-    return bl;
+  // Block ids of this wave's rows at `step` (wave-uniform scalar loads);
+  // clamping the key first keeps every clamped row's block.
+  auto fetch = [&](int step) __attribute__((always_inline)) {
+    Blocks b;
+    b.lo = table[min(step * KT + rg * 16, kmax - 1) / BS];
+    b.hi = BS >= 16 ? b.lo : table[min(step * KT + rg * 16 + 8, kmax - 1) / BS];
+    return b;
   };
-  auto issue = [&](int step, const Blocks& bl, char* kdst, char* vdst) {
+  auto issue = [&](const char* base, int step, const Blocks& bl, char* dst) __attribute__((always_inline)) {
+    const int key = min(step * KT + lrow, kmax - 1);
+    const int64_t blk = (BS >= 16 || (lane >> 2) < 8) ? bl.lo : bl.hi;
+    const char* src = base + (blk * BS + (key & (BS - 1))) * ROWB + lchunk;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int row0 = wave * WROWS + i * RPL;
-      const int row = row0 + lane / DCH;
-      const int key = min(step * KT + row, kmax - 1);
-      const int64_t blk = bl.b[NBW > 1 ? i * RPL / BS : 0];
-      const int64_t off = (blk * BS + (key & (BS - 1))) * ROWB + (((lane % DCH) ^ swz<DCH>(row)) * 16);
-      load_to_lds(kbase + off, kdst + row0 * ROWB);
-      load_to_lds(vbase + off, vdst + row0 * ROWB);
-    }
+    for (int i = 0; i < LPW; ++i)
+      load_to_lds(src + (cg0 + i) * 64, dst + (cg0 + i) * (KT * 64) + rg * 1024);
   };
 
   float m = -INFINITY, lsum = 0.0f;
   floatx16_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = floatx16_t{};
+  floatx16_t st[NT];  // scores of the step whose softmax is next
+  vec pb[NT][2];      // probabilities of the step whose PV is next
 
-  // Transposing-read geometry: this lane, as source lane 4*k4 + q4 of its
-  // 16-lane group g16, addresses row 4*(g16/2) + k4 (+8) of a 16-key slice,
-  // dims dt*32 + (g16%2)*16 + 4*q4 + [0,4).
+  // Read geometry.  MFMA operand of K: row n*32 + li, chunk 2*ks + h, i.e.
+  // column ks/2 at a per-lane base that depends on ks % 2.  Transposing read
+  // of V: this lane, as source lane 4*k4 + q4 of its 16-lane group g16,
+  // addresses row 4*(g16/2) + k4 (+8) of a 16-key slice, dims
+  // dt*32 + (g16%2)*16 + 4*q4 + [0,4): column dt at a per-lane base.
+  const int kb_even = tile_off<KT>(li, h), kb_odd = tile_off<KT>(li, 2 + h);
   const int g16 = lane >> 4, k4 = (lane >> 2) & 3, q4 = lane & 3;
-  const int vrow = 4 * (g16 >> 1) + k4;
-  const int vsw_lo = swz<DCH>(vrow), vsw_hi = swz<DCH>(vrow + 8);  // the same for + 16 s + 32 n
+  const int vrow = 4 * (g16 >> 1) + k4, vch = (g16 & 1) * 2 + (q4 >> 1);
+  const int vb_lo = tile_off<KT>(vrow, vch) + (q4 & 1) * 8, vb_hi = tile_off<KT>(vrow + 8, vch) + (q4 & 1) * 8;
 
-  // One step: attend to the tile in (kt, vt) while the next step's tile
-  // streams into (kn, vn).
-  Blocks next = fetch(0);
-  auto step_body = [&](int step, const char* kt, const char* vt, char* kn, char* vn) {
-    if (step + 1 < nsteps) issue(step + 1, next, kn, vn);
-    const int key0 = step * KT;
-
-    // S^T = K Q^T: NT tiles of 32 keys x this wave's 32 rows.  The lane holds
-    // keys n*32 + 8*(v/4) + 4*h + v%4 of row li.
-    floatx16_t st[NT];
+  // MFMA unit: S^T = K Q^T for the next step from tile kt (keys on the MFMA
+  // row axis: the lane holds keys n*32 + 8*(v/4) + 4*h + v%4 of row li) and,
+  // with PV, O^T += V^T P^T for this step from tile vt.  The V^T operand for
+  // dims dt*32 + li and the 8 keys of P's slots comes from two transposing
+  // reads (rows vrow and vrow + 8 of the 16-key slice).  Operands are read
+  // into arrays and the instruction groups are ordered explicitly so that
+  // LDS reads run one group of MFMAs ahead instead of each MFMA waiting for
+  // its own read.
+  auto gemm = [&](auto with_pv, const char* kt, const char* vt) __attribute__((always_inline)) {
+    constexpr bool kPV = decltype(with_pv)::value;
+    vec ka[NT][KS];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[n][ks] = *reinterpret_cast<const vec*>(kt + (ks >> 1) * (KT * 64) + n * 32 * 64 +
+                                                  ((ks & 1) ? kb_odd : kb_even));
+    vec va[NT][2][DT];
+    if constexpr (kPV) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const char* vs = vt + (n * 32 + s2 * 16) * 64 + dt * (KT * 64);
+            const uint2 lo = lds_read_tr(vs + vb_lo);
+            const uint2 hi = lds_read_tr(vs + vb_hi);
+            va[n][s2][dt] = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          }
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       st[n] = floatx16_t{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const vec a =
-            *reinterpret_cast<const vec*>(kt + (n * 32 + li) * ROWB + (((ks * 2 + h) ^ swz<DCH>(li)) * 16));
-        st[n] = M::mma(a, qb[ks], st[n]);
-      }
+      for (int ks = 0; ks < KS; ++ks) st[n] = M::mma(ka[n][ks], qb[ks], st[n]);
     }
-    next = fetch(step + 2);
+    if constexpr (kPV) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt] = M::mma(va[n][s2][dt], pb[n][s2], o[dt]);
+    }
+    // Order: K reads of tile 0; tile-0 MFMAs each followed by one K read of
+    // tile 1; with PV, tile-1 MFMAs each followed by two transposing reads,
+    // then the first half of the PV MFMAs each followed by two more, then the
+    // rest.  (Masks: 0x100 LDS read, 0x008 MFMA.)
+    static_assert(NT == 2 && 4 * DT == 2 * KS, "schedule shape");
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (kPV) {
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);
+    }
+  };
 
-    // Online softmax on unscaled scores (for scale > 0 the max commutes with
-    // the scale, which is folded into the exponent).
+  // Softmax unit j: online softmax of step j's scores into P_j.  Scores are
+  // unscaled (for scale > 0 the max commutes with the scale, which is folded
+  // into the exponent).  P^T slots 0..7 for 16-key slice (n, s) are keys
+  // n*32 + 16s + 4h + [0,4) and n*32 + 16s + 8 + 4h + [0,4): score values
+  // 8s .. 8s+7 of tile n.
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int key0 = j * KT;
     if (scale_log2 <= 0.0f) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) st[n] *= scale_log2;
@@ -283,11 +355,6 @@ __global__ void __launch_bounds__(kPrefillThreads)
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     }
     const float ms = (m == -INFINITY) ? 0.0f : m;
-
-    // P^T operand for 16-key slice (n, s): slots 0..7 of this lane are keys
-    // n*32 + 16s + 4h + [0,4) and n*32 + 16s + 8 + 4h + [0,4), i.e. its score
-    // values 8s .. 8s+7 of tile n.
-    vec pb[NT][2];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
 #pragma unroll
@@ -304,46 +371,74 @@ __global__ void __launch_bounds__(kPrefillThreads)
         pb[n][s2] = __builtin_bit_cast(vec, raw);
       }
     }
-
-    // O^T += V^T P^T.  The V^T operand for dims dt*32 + li and the same 8 keys
-    // comes from two transposing reads (rows vrow and vrow + 8 of the slice).
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int rw = n * 32 + s2 * 16 + vrow;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int ch = dt * 4 + (g16 & 1) * 2 + (q4 >> 1);
-          const uint2 lo = lds_read_tr(vt + rw * ROWB + (ch ^ vsw_lo) * 16 + (q4 & 1) * 8);
-          const uint2 hi = lds_read_tr(vt + (rw + 8) * ROWB + (ch ^ vsw_hi) * 16 + (q4 & 1) * 8);
-          const vec a = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          o[dt] = M::mma(a, pb[n][s2], o[dt]);
-        }
-      }
-    }
-
-    wait_loads_to_lds();
-    __syncthreads();
   };
 
-  issue(0, next, lk0, lv0);
-  next = fetch(1);
+  // Schedule.  Every wave runs the same units: gemm(-1), softmax(0),
+  // gemm(0), softmax(1), ..., softmax(n-1), gemm(n-1), each closed by a
+  // barrier.  Group B passes one extra barrier first, so it runs unit u in
+  // phase u + 1 while group A runs it in phase u: in every phase one wave of
+  // each SIMD feeds the matrix core and the other runs the softmax on the
+  // vector ALU.  (A barrier counts arrivals, not which instruction arrives.)
+  // gemm(j-1) reads K_j and V_{j-1}.  Round m = phases 2m and 2m+1: at the
+  // start of round m every wave issues its share of K_{m+1} and V_m into the
+  // buffers that round m-1 finished reading, and waits for them at the end
+  // of the round.  Group A issues round j with its gemm(j-1); group B issues
+  // round j+1 with its softmax(j) (round 0 before its extra barrier).
+  Blocks blk_v = fetch(0);  // block ids of the V tile of the next round
+  Blocks blk_k = fetch(1);  // ... and of its K tile
+  auto issue_round = [&](int mr, char* kw, char* vw) __attribute__((always_inline)) {
+    if (mr + 1 < nsteps) issue(kbase, mr + 1, blk_k, kw);
+    if (mr < nsteps) issue(vbase, mr, blk_v, vw);
+    blk_v = blk_k;
+    blk_k = fetch(mr + 2);
+  };
+  issue(kbase, 0, blk_v, lds[0]);
   wait_loads_to_lds();
-  __syncthreads();
-  for (int step = 0; step < nsteps; step += 2) {
-    step_body(step, lk0, lv0, lk1, lv1);
-    if (step + 1 >= nsteps) break;
-    step_body(step + 1, lk1, lv1, lk0, lv0);
+  barrier_keep_loads();
+  if (group_b) {
+    issue_round(0, lds[1], lds[2]);
+    barrier_keep_loads();
   }
+  // gemm(-1): scores of step 0 only.
+  gemm(std::false_type{}, lds[0], lds[3]);
+  if (!group_b) issue_round(0, lds[1], lds[2]);
+  if (group_b) wait_loads_to_lds();
+  barrier_keep_loads();
+  // Step j's units: gemm(j-1), then softmax(j) unless j == n.  k_rd / v_rd:
+  // the buffers gemm(j-1) reads (K_j, V_{j-1}; at j == n the K tile is stale
+  // and its scores unused); A writes K_{j+1}, V_j into (ka, va) right after
+  // issuing its reads; B writes K_{j+2}, V_{j+1} into (k_rd, v_rd) once
+  // both groups have finished gemm(j-1).  Issuing after the reads keeps the
+  // compiler from waiting for these loads before them.
+  auto softmax_unit = [&](int j, char* kb, char* vb) __attribute__((always_inline)) {
+    if (group_b) issue_round(j + 1, kb, vb);
+    softmax(j);
+    if (!group_b) wait_loads_to_lds();
+    barrier_keep_loads();
+  };
+  softmax_unit(0, lds[0], lds[3]);
+  auto body = [&](int j, char* k_rd, char* v_rd, char* ka, char* va) __attribute__((always_inline)) {
+    gemm(std::true_type{}, k_rd, v_rd);
+    if (!group_b) issue_round(j, ka, va);
+    if (group_b) wait_loads_to_lds();
+    barrier_keep_loads();
+    if (j == nsteps) return;
+    softmax_unit(j, k_rd, v_rd);
+  };
+  for (int j = 1; j <= nsteps; j += 2) {
+    body(j, lds[1], lds[2], lds[0], lds[3]);
+    if (j + 1 > nsteps) break;
+    body(j + 1, lds[0], lds[3], lds[1], lds[2]);
+  }
+  if (!group_b) barrier_keep_loads();
 
-  // Normalise; stage the wave's 32 x D output rows in LDS (wave w takes one
-  // of the four tile arrays, no longer read) and write whole rows.  The lane
-  // holds dims dt*32 + 8*j + 4*h + [0,4) of row li, j = 0..3; chunk c of row
-  // rr is stored at chunk position c ^ (rr % DCH).
+  // Normalise; stage the wave's 32 x D output rows in LDS (two waves per
+  // tile array, no longer read) and write whole rows.  The lane holds dims
+  // dt*32 + 8*j + 4*h + [0,4) of row li, j = 0..3; chunk c of row rr is
+  // stored at chunk position c ^ (rr % DCH).
   const float lt = sum_halves(lsum);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  char* ob = wave == 0 ? lk0 : wave == 1 ? lv0 : wave == 2 ? lk1 : lv1;
+  char* ob = &lds[wave >> 1][(wave & 1) * kRowsPerWave * ROWB];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
