@@ -39,9 +39,12 @@ constexpr float kNegInf = -INFINITY;
 #define PA_DECODE_NT 0
 #endif
 
-// Unit = NLD wave loads of K and V (TPW tokens each).  Few query heads per
-// KV head: short units, 4 in flight per wave.  Many heads (more arithmetic
-// per byte): longer units for more independent work per lane, 2 in flight.
+// Unit = NLD wave loads of K and V (TPW tokens each), 2 units in flight per
+// wave.  Few query heads per KV head: short units.  Many heads (more
+// arithmetic per byte): longer units for more independent work per lane.
+// More loads in flight do not raise the streaming rate; they lengthen the
+// queues, and the kernel's final loads then wait that much longer (measured:
+// 4 units in flight cost ~0.8 us more per launch than 2 on a 75 MB decode).
 template <typename E, int D, int BS, int G>
 struct DecodeShape {
   static constexpr int S = E::bytes;
@@ -52,7 +55,7 @@ struct DecodeShape {
   static constexpr int NLD = (BS / TPW) < NLD_MAX ? (BS / TPW) : NLD_MAX;  // loads per unit per side
   static constexpr int U = NLD * TPW;                            // tokens per unit
   static constexpr int UPB = BS / U;                             // units per block
-  static constexpr int RING = G <= 2 ? 4 : 2;                    // units in flight per wave
+  static constexpr int RING = 2;                                 // units in flight per wave
   static_assert(BS % TPW == 0, "block size must hold whole wave loads");
   static_assert(BS % U == 0, "units tile a block");
 };
