@@ -6,15 +6,18 @@ Workload: the Qwen3-1.7B-shaped decode layer -- B=32 sequences, 16 query /
 8 KV heads, head_dim 128, 16-token blocks, contexts uniform in [512, 640],
 a 1,378-block (22,048-token) pool per layer, bf16.  One step = the step's
 append (one new token per sequence) + paged decode attention, on resident
-device inputs.  The pool holds 28 layers sharing one block table and each
-step works on the next layer, as a model's layer loop does, so every step
-reads its K/V from HBM rather than from the 256 MB Infinity Cache.
+device inputs, run as one pa_decode_append launch (the separate append and
+decode launches are timed too, as ``unfused_step_ms``).  The pool holds 28
+layers sharing one block table and each step works on the next layer, as a
+model's layer loop does, so every step reads its K/V from HBM rather than
+from the 256 MB Infinity Cache.
 
 Prints one JSON line.  ``value`` is decode KV-read GB/s over the whole step
-(append + decode); ``roofline`` rates the decode kernel alone; the second
-half of the metric, attention tokens/s at B=64, is measured on the 13B-shaped
-B=64 workload and reported as ``attention_tok_s_b64``.  ``rows`` gives the
-other hot-path rows on the workloads that exercise them.
+(append + decode); ``roofline`` rates the step's one kernel (the fused
+append + decode) on its algorithmic bytes; the second half of the metric,
+attention tokens/s at B=64, is measured on the 13B-shaped B=64 workload and
+reported as ``attention_tok_s_b64``.  ``rows`` gives the other hot-path rows
+on the workloads that exercise them.
 """
 
 import argparse
@@ -92,14 +95,15 @@ def prefill_flops(T, H_q, d, ctx_before):
 
 # ------------------------------------------------------------------ timing
 
-def time_loop(torch, fn, iters, warmup):
+def time_loop(torch, fn, iters, warmup, replays=5):
     """Average ms per call of fn(i) over ``iters`` consecutive calls.
 
     ``warmup`` eager calls first; then the ``iters`` calls are captured in one
     HIP graph (the library enqueues plain kernel launches, no memsets), the
-    graph is replayed once untimed, and one more replay is timed with events
-    on the current stream.  A graph keeps the host's per-call marshalling
-    (tens of microseconds of Python) out of kernels that take ~10 us.
+    graph is replayed once untimed, and then ``replays`` more times, each
+    timed with events on the current stream; the median replay is reported.
+    A graph keeps the host's per-call marshalling (tens of microseconds of
+    Python) out of kernels that take ~10 us.
     """
     for i in range(warmup):
         fn(i)
@@ -110,14 +114,17 @@ def time_loop(torch, fn, iters, warmup):
             fn(warmup + i)
     g.replay()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / iters)
     del g
-    return a.elapsed_time(b) / iters
+    return sorted(times)[len(times) // 2]
 
 
 def main():
@@ -166,6 +173,10 @@ def main():
 
     def full_step(i):
         gpu.layer = i % L
+        gpu.launch(si, fused=True)
+
+    def unfused_step(i):
+        gpu.layer = i % L
         gpu.launch(si)
 
     def decode_only(i):
@@ -176,11 +187,14 @@ def main():
         gpu.layer = i % L
         gpu.launch(si, do_decode=False, do_prefill=False)
 
+    assert si.fusable and si.n_pairs == 0  # the step is exactly one fused launch
     ms_step = time_loop(torch, full_step, args.steps, args.warmup)
+    ms_unfused = time_loop(torch, unfused_step, args.steps, args.warmup)
     ms_decode = time_loop(torch, decode_only, args.steps, args.warmup)
     ms_append = time_loop(torch, append_only, args.steps, args.warmup)
     value = dbytes / (ms_step * 1e-3) / 1e9
-    achieved = dbytes / (ms_decode * 1e-3) / 1e9
+    kernel_bytes = dbytes + abytes  # the fused kernel also reads the new rows and writes them into the pool
+    achieved = kernel_bytes / (ms_step * 1e-3) / 1e9
     plan_ws = pa.pa_decode_workspace_size(gpu.pool, len(lens), cfg["H_q"], int(lens.max()))
     del gpu, si
     torch.cuda.empty_cache()
@@ -204,9 +218,13 @@ def main():
             "B": 32, "H_q": 16, "H_kv": 8, "head_dim": 128, "block_size": 16, "pool_blocks": 1378,
             "layers_rotated": L, "seed": 0,
         },
+        "timing": "HIP graph of K steps replayed 5 times after W eager warmup steps and one untimed replay; "
+                  "each replay timed with events, the median replay reported",
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "unfused_step_ms": round(ms_unfused, 5),
         "decode_ms": round(ms_decode, 5),
         "append_ms": round(ms_append, 5),
+        "decode_only_GBps": round(dbytes / (ms_decode * 1e-3) / 1e9, 1),
         "decode_bytes": dbytes,
         "decode_split_workspace_bytes": plan_ws,
         "roofline": {
@@ -216,8 +234,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(),
-            "kernel": "pa::decode_kernel<BF16,128,2,16,1024>",
-            "per_launch_bytes": dbytes,
+            "kernel": "pa::decode_kernel<BF16,128,2,16,1024> (pa_decode_append: append + decode)",
+            "per_launch_bytes": kernel_bytes,
         },
     }
 
@@ -226,7 +244,7 @@ def main():
     g3 = GpuRun(scn3, device=dev, num_layers=1, fill="randn")
     g3.run_setup()
     si3 = g3.prepare(scn3.steps[0])
-    ms3 = time_loop(torch, lambda i: g3.launch(si3), max(20, args.steps // 4), 5)
+    ms3 = time_loop(torch, lambda i: g3.launch(si3, fused=True), max(20, args.steps // 4), 5)
     ms3d = time_loop(torch, lambda i: g3.launch(si3, do_copy=False, do_append=False), max(20, args.steps // 4), 5)
     lens3 = si3.lens.cpu().numpy()
     b3 = decode_bytes(lens3, 40, 40, 128, 16, 2)

@@ -123,6 +123,29 @@ int pa_decode(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, i
               float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * One decode step in one launch: each sequence's new token is appended and
+ * then attended to with the rest of its context ([icarus] "Block Table 如何
+ * 工作": the new token's K/V go into the current block, and the query reads
+ * every visible block).  Same result, pool contents included, as
+ * pa_cache_append(pool, layer, k_new, v_new, slot_mapping, B) followed by
+ * pa_decode(pool, layer, out, q, B, ...).
+ *   k_new, v_new: device [B][num_kv_heads][head_dim], pool dtype, 16-byte
+ *        aligned: sequence b's new token.
+ *   slot_mapping: device int32 [B]; slot_mapping[b] is the slot of position
+ *        context_lens[b] - 1 in row b of block_tables (what the block manager
+ *        returns for a one-token append), or negative to skip that write
+ *        (then the pool's own row at that position is read, as pa_decode
+ *        would).  The slot's block must not be shared with another sequence
+ *        (copy-on-write copies come first).
+ *   context_lens: include the new token (>= 1).
+ *   Everything else as pa_decode, workspace size included.
+ */
+int pa_decode_append(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, const void* k_new,
+                     const void* v_new, const int32_t* slot_mapping, int32_t B, int32_t H_q,
+                     const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t max_ctx,
+                     float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Causal prefill chunk over paged K/V: a long prompt is processed in chunks
  * ([ttlab] "새 문제: 긴 프리필이 디코드를 멈춘다"); chunk row t sits at position
  * ctx_before + t and attends to positions 0 .. ctx_before + t of its own

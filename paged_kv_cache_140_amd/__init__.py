@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     pa_cache_append,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_append,
     pa_decode_workspace_size,
     pa_prefill_chunk,
 )

@@ -109,6 +109,31 @@ def pa_decode(pool, layer, out, q, block_tables, context_lens, max_ctx, scale, w
                           _ptr(workspace), ws_bytes, _stream(stream)), "pa_decode")
 
 
+def pa_decode_append(pool, layer, out, q, k_new, v_new, slot_mapping, block_tables, context_lens, max_ctx, scale,
+                     workspace=None, stream=None):
+    """One decode step in one launch: append each sequence's new token
+    (k_new/v_new [B][H_kv][d] at slot_mapping [B]), then decode."""
+    B, H_q, d = (int(x) for x in q.shape)
+    _need(q, "q", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(out, "out", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(k_new, "k_new", pool.torch_dtype, (B, pool.num_kv_heads, pool.head_dim))
+    _need(v_new, "v_new", pool.torch_dtype, (B, pool.num_kv_heads, pool.head_dim))
+    _need(slot_mapping, "slot_mapping", torch.int32, (B,))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B][max_blocks]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    s = pool.struct()
+    check(lib().pa_decode_append(ctypes.byref(s), layer, _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                 _ptr(slot_mapping), B, H_q, _ptr(block_tables), int(block_tables.shape[1]),
+                                 _ptr(context_lens), int(max_ctx), float(scale), _ptr(workspace), ws_bytes,
+                                 _stream(stream)), "pa_decode_append")
+
+
 def pa_prefill_chunk(pool, layer, out, q, block_table, ctx_before, scale, stream=None):
     T, H_q, d = (int(x) for x in q.shape)
     _need(q, "q", pool.torch_dtype, (T, H_q, pool.head_dim))

@@ -24,6 +24,11 @@
 //    LDS.
 //  * a sequence split over several partitions writes (m, l, acc) partials
 //    to the workspace and a small merge kernel combines them.
+//  * fused append (pa_decode_append, FUSED): the step's new token of each
+//    sequence, at position ctx - 1, is written into its slot by the
+//    workgroup whose partition holds that position; that workgroup's paged
+//    pass stops at ctx - 1 and one wave adds the new token from the input,
+//    so no read waits on the write.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -109,13 +114,14 @@ struct QChunk<F32> {
 };
 
 
-template <typename E, int D, int G, int BS, int MAXT>
+template <typename E, int D, int G, int BS, int MAXT, bool FUSED>
 __global__ void __launch_bounds__(MAXT)
-    decode_kernel(const char* __restrict__ pool_k, const char* __restrict__ pool_v, int64_t layer_off,
-                  int64_t head_stride, const char* __restrict__ q, void* __restrict__ out,
-                  const int32_t* __restrict__ block_tables, int32_t max_blocks,
-                  const int32_t* __restrict__ context_lens, float scale_log2, int32_t H_q, int32_t blocks_per_part,
-                  int32_t num_parts, float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
+    decode_kernel(char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off, int64_t head_stride,
+                  const char* __restrict__ q, void* __restrict__ out, const int32_t* __restrict__ block_tables,
+                  int32_t max_blocks, const int32_t* __restrict__ context_lens, float scale_log2, int32_t H_q,
+                  int32_t blocks_per_part, int32_t num_parts, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+                  const char* __restrict__ k_new, const char* __restrict__ v_new,
+                  const int32_t* __restrict__ new_slots) {
   using Sh = DecodeShape<E, D, BS, G>;
   constexpr int S = Sh::S, VEC = Sh::VEC, LPT = Sh::LPT, TPW = Sh::TPW, NLD = Sh::NLD, U = Sh::U, UPB = Sh::UPB,
                 RING = Sh::RING;
@@ -158,6 +164,26 @@ __global__ void __launch_bounds__(MAXT)
   }
   const int j1 = min(j0 + blocks_per_part, nblk);
 
+  // Fused append: this sequence's new token sits at position ctx - 1.  The
+  // partition holding that position masks that position out of its paged
+  // pass (vis = ctx - 1: the pool row may be read, stale, but never counts),
+  // and wave 0 adds the new token from the input at the end and writes it
+  // into its slot.  The unit walk itself stays that of a plain decode, so
+  // the first K/V loads do not wait for the slot.  A negative slot writes
+  // nothing and reads the pool's own row, as a plain decode would.
+  int vis = ctx;
+  bool owns_new = false;
+  int new_slot = -1;
+  uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+  if constexpr (FUSED) {
+    new_slot = __builtin_amdgcn_readfirstlane(new_slots[b]);
+    owns_new = new_slot >= 0 && (ctx - 1) / BS >= j0 && (ctx - 1) / BS < j1;
+    const int64_t new_row = (static_cast<int64_t>(b) * gridDim.y + g) * D * S;  // [B][H_kv][D] inputs
+    kx = load16(k_new + new_row + c * 16);  // every lane: a fixed number of loads keeps the waits exact
+    vx = load16(v_new + new_row + c * 16);
+    if (owns_new) vis = ctx - 1;
+  }
+
   QChunk<E> qc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) qc[h].set(load16(q + ((head0 + h) * D + c * VEC) * S));
@@ -199,7 +225,7 @@ __global__ void __launch_bounds__(MAXT)
     float s[NLD][G];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const bool dead = masked && tok0 + i * TPW >= ctx;
+      const bool dead = masked && tok0 + i * TPW >= vis;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float d = group_sum<LPT>(qc[h].dot(kr[i])) * scale_log2;
@@ -234,7 +260,7 @@ __global__ void __launch_bounds__(MAXT)
     for (int i = 0; i < NLD; ++i) {
       float vf[VEC];
       widen(E{}, vr[i], vf);
-      if (masked && tok0 + i * TPW >= ctx) {
+      if (masked && tok0 + i * TPW >= vis) {
         // unused slots may hold anything (NaN included): select, not multiply
 #pragma unroll
         for (int e = 0; e < VEC; ++e) vf[e] = 0.0f;
@@ -249,11 +275,55 @@ __global__ void __launch_bounds__(MAXT)
     }
   };
 
+  // Fused: the new token's share of the attention, added by wave 0 of the
+  // partition that holds it, right after the wave's first K/V loads are in
+  // flight (so its own input load overlaps them).  Row 0 of the wave's lane
+  // rows holds it; the other rows take no part (score -inf, value 0).
+  auto add_new_token = [&]() {
+    if constexpr (FUSED) {
+      if (owns_new && wave == 0) {
+        float sx[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float d = group_sum<LPT>(qc[h].dot(kx)) * scale_log2;
+          sx[h] = r == 0 ? d : kNegInf;
+        }
+        bool grew = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) grew |= sx[h] > m[h];
+        if (__any(grew)) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float mx = fmaxf(m[h], sx[h]);
+            const float alpha = exp2_fast(m[h] - ((mx == kNegInf) ? 0.0f : mx));
+            m[h] = mx;
+            l[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
+          }
+        }
+        float vf[VEC];
+        widen(E{}, vx, vf);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) vf[e] = r == 0 ? vf[e] : 0.0f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float p = exp2_fast(sx[h] - ((m[h] == kNegInf) ? 0.0f : m[h]));
+          l[h] += p;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        }
+      }
+    }
+  };
+
   // Units of this partition: full ones [u_first, u_full), stepping by W per
   // wave, streamed through a ring of RING loads in flight; then at most one
   // partly visible unit, handled by the wave that owns it.
   const int u_stop = min(j1 * UPB, (ctx + U - 1) / U);
   const int u_full = min(u_stop, ctx / U);
+  // A full unit that holds the masked-out new token (fused, ctx % U == 0).
+  const int u_mask = FUSED && owns_new && ctx % U == 0 ? (ctx - 1) / U : -1;
   const int u_first = u_begin + wave;
   const int n_w = u_full > u_first ? (u_full - u_first + W - 1) / W : 0;  // this wave's full units
   // The partly visible last unit (if this partition has it) is loaded first,
@@ -277,11 +347,15 @@ __global__ void __launch_bounds__(MAXT)
       const int u = u_first + min(p, n_w - 1) * W;
       load_unit(u, kr[p], vr[p], p < n_w ? ph[p] : btrow[u / UPB]);
     }
+    add_new_token();
     for (int k = 0; k < n_w; k += RING) {
 #pragma unroll
       for (int p = 0; p < RING; ++p) {
         const int idx = k + p;
-        if (idx < n_w) process(u_first + idx * W, kr[p], vr[p], false);
+        if (idx < n_w) {
+          const int u = u_first + idx * W;
+          process(u, kr[p], vr[p], FUSED && u == u_mask);
+        }
         // Keep refills in ring order: the in-order load counter then only
         // ever waits for the oldest slot.
         __builtin_amdgcn_sched_barrier(0);
@@ -291,6 +365,7 @@ __global__ void __launch_bounds__(MAXT)
       }
     }
   }
+  if (n_w <= 0) add_new_token();
   if (has_tail) process(u_full, kt, vt, true);
 
   // Merge the TPW row groups of this wave (lanes LPT, 2*LPT, ... apart hold
@@ -353,6 +428,17 @@ __global__ void __launch_bounds__(MAXT)
         ws_ml[2 * slot] = mx;
         ws_ml[2 * slot + 1] = lt;
       }
+    }
+  }
+
+  if constexpr (FUSED) {
+    // The new token's row into its slot, last: nothing in this launch reads
+    // it back, and a barrier after these stores would wait for them.
+    if (owns_new && wave == 0 && r == 0) {
+      const int64_t dst =
+          layer_off + static_cast<int64_t>(g) * head_stride + static_cast<int64_t>(new_slot) * D * S + c * 16;
+      *reinterpret_cast<uint4*>(pool_k + dst) = kx;
+      *reinterpret_cast<uint4*>(pool_v + dst) = vx;
     }
   }
 }
@@ -480,18 +566,27 @@ static Workspace carve(void* ws, const DecodePlan& pl, int B, int H_kv, int H_q)
   return w;
 }
 
-template <typename E, int D, int G, int BS>
+// New tokens of a fused append: [B][H_kv][D] rows and their slots, or all
+// NULL for a plain decode.
+struct NewTokens {
+  const void* k;
+  const void* v;
+  const int32_t* slots;
+};
+
+template <typename E, int D, int G, int BS, bool FUSED>
 static void launch_decode(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B, int32_t H_q,
                           const int32_t* bt, int32_t max_blocks, const int32_t* ctx, float scale_log2,
-                          const DecodePlan& pl, const Workspace& ws, hipStream_t stream) {
+                          const DecodePlan& pl, const Workspace& ws, const NewTokens& nt, hipStream_t stream) {
   const int64_t head_stride = static_cast<int64_t>(pool->num_blocks) * BS * D * E::bytes;
   const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * head_stride;
   const size_t lds = static_cast<size_t>(pl.waves) * G * (D + 2) * sizeof(float);
   dim3 grid(pl.num_parts, pool->num_kv_heads, B);
-  hipLaunchKernelGGL((decode_kernel<E, D, G, BS, max_threads<G>()>), grid, dim3(64 * pl.waves), lds, stream,
-                     static_cast<const char*>(pool->k), static_cast<const char*>(pool->v), layer_off, head_stride,
+  hipLaunchKernelGGL((decode_kernel<E, D, G, BS, max_threads<G>(), FUSED>), grid, dim3(64 * pl.waves), lds, stream,
+                     static_cast<char*>(pool->k), static_cast<char*>(pool->v), layer_off, head_stride,
                      static_cast<const char*>(q), out, bt, max_blocks, ctx, scale_log2, H_q, pl.blocks_per_part,
-                     pl.num_parts, ws.ml, ws.acc);
+                     pl.num_parts, ws.ml, ws.acc, static_cast<const char*>(nt.k), static_cast<const char*>(nt.v),
+                     nt.slots);
   if (pl.num_parts > 1) {
     hipLaunchKernelGGL((decode_merge_kernel<E, D>), dim3(static_cast<uint32_t>(B) * H_q), dim3(D),
                        pl.num_parts * sizeof(float), stream, out, ws.ml, ws.acc, ctx, H_q, pl.num_parts,
@@ -500,40 +595,44 @@ static void launch_decode(const pa_kv_pool* pool, int32_t layer, void* out, cons
 }
 
 using DecodeFn = void (*)(const pa_kv_pool*, int32_t, void*, const void*, int32_t, int32_t, const int32_t*, int32_t,
-                          const int32_t*, float, const DecodePlan&, const Workspace&, hipStream_t);
+                          const int32_t*, float, const DecodePlan&, const Workspace&, const NewTokens&, hipStream_t);
 
+template <typename E, int D, int G, int BS>
+static DecodeFn pick_fused(bool fused) {
+  return fused ? &launch_decode<E, D, G, BS, true> : &launch_decode<E, D, G, BS, false>;
+}
 template <typename E, int D, int G>
-static DecodeFn pick_bs(int bs) {
+static DecodeFn pick_bs(int bs, bool fused) {
   switch (bs) {
-    case 8: return &launch_decode<E, D, G, 8>;
-    case 16: return &launch_decode<E, D, G, 16>;
-    case 32: return &launch_decode<E, D, G, 32>;
+    case 8: return pick_fused<E, D, G, 8>(fused);
+    case 16: return pick_fused<E, D, G, 16>(fused);
+    case 32: return pick_fused<E, D, G, 32>(fused);
   }
   return nullptr;
 }
 template <typename E, int D>
-static DecodeFn pick_g(int G, int bs) {
+static DecodeFn pick_g(int G, int bs, bool fused) {
   switch (G) {
-    case 1: return pick_bs<E, D, 1>(bs);
-    case 2: return pick_bs<E, D, 2>(bs);
-    case 4: return pick_bs<E, D, 4>(bs);
-    case 8: return pick_bs<E, D, 8>(bs);
+    case 1: return pick_bs<E, D, 1>(bs, fused);
+    case 2: return pick_bs<E, D, 2>(bs, fused);
+    case 4: return pick_bs<E, D, 4>(bs, fused);
+    case 8: return pick_bs<E, D, 8>(bs, fused);
   }
   return nullptr;
 }
 template <typename E>
-static DecodeFn pick_d(int D, int G, int bs) {
+static DecodeFn pick_d(int D, int G, int bs, bool fused) {
   switch (D) {
-    case 64: return pick_g<E, 64>(G, bs);
-    case 128: return pick_g<E, 128>(G, bs);
+    case 64: return pick_g<E, 64>(G, bs, fused);
+    case 128: return pick_g<E, 128>(G, bs, fused);
   }
   return nullptr;
 }
-static DecodeFn pick(int dtype, int D, int G, int bs) {
+static DecodeFn pick(int dtype, int D, int G, int bs, bool fused) {
   switch (dtype) {
-    case PA_F32: return pick_d<F32>(D, G, bs);
-    case PA_BF16: return pick_d<BF16>(D, G, bs);
-    case PA_F16: return pick_d<F16>(D, G, bs);
+    case PA_F32: return pick_d<F32>(D, G, bs, fused);
+    case PA_BF16: return pick_d<BF16>(D, G, bs, fused);
+    case PA_F16: return pick_d<F16>(D, G, bs, fused);
   }
   return nullptr;
 }
@@ -550,32 +649,55 @@ extern "C" size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t B, in
   return workspace_bytes_for(pl, B, pool->num_kv_heads, H_q, pool->head_dim);
 }
 
+namespace pa {
+static int decode_entry(const char* who, const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B,
+                        int32_t H_q, const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                        int32_t max_ctx, float scale, void* workspace, size_t workspace_bytes, const NewTokens& nt,
+                        hipStream_t stream) {
+  const std::string w(who);
+  if (int e = check_pool(pool, layer)) return e;
+  if (B < 0 || H_q <= 0 || max_blocks < 0 || max_ctx < 0) return fail(PA_EINVAL, w + ": negative size");
+  if (B == 0) return PA_OK;
+  if (!out || !q || !block_tables || !context_lens) return fail(PA_EINVAL, w + ": NULL argument");
+  if (H_q % pool->num_kv_heads) return fail(PA_EINVAL, w + ": H_q must be a multiple of num_kv_heads");
+  if (static_cast<int64_t>(max_blocks) * pool->block_size < max_ctx)
+    return fail(PA_EINVAL, w + ": max_blocks * block_size < max_ctx");
+  if (!aligned16(q) || !aligned16(pool->k) || !aligned16(pool->v))
+    return fail(PA_EINVAL, w + ": q and pool must be 16-byte aligned");
+  if (nt.slots && (!aligned16(nt.k) || !aligned16(nt.v)))
+    return fail(PA_EINVAL, w + ": k_new and v_new must be 16-byte aligned");
+  if (B > 65535 || pool->num_kv_heads > 65535) return fail(PA_EINVAL, w + ": grid too large");
+  const int G = H_q / pool->num_kv_heads;
+  DecodeFn fn = pick(pool->dtype, pool->head_dim, G, pool->block_size, nt.slots != nullptr);
+  if (!fn) return fail(PA_ENOTSUP, w + ": (dtype, head_dim, block_size, H_q/H_kv) not compiled");
+  DecodePlan pl = plan_decode(B, pool->num_kv_heads, G, pool->block_size, max_ctx);
+  const size_t need = workspace_bytes_for(pl, B, pool->num_kv_heads, H_q, pool->head_dim);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ESPACE, w + ": workspace of " + std::to_string(need) + " bytes needed");
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u))
+    return fail(PA_EINVAL, w + ": workspace must be 4-byte aligned");
+  Workspace ws = carve(workspace, pl, B, pool->num_kv_heads, H_q);
+  const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  fn(pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens, scale_log2, pl, ws, nt, stream);
+  return check_launch(who);
+}
+}  // namespace pa
+
 extern "C" int pa_decode(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B, int32_t H_q,
                          const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
                          int32_t max_ctx, float scale, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-  using namespace pa;
-  if (int e = check_pool(pool, layer)) return e;
-  if (B < 0 || H_q <= 0 || max_blocks < 0 || max_ctx < 0) return fail(PA_EINVAL, "pa_decode: negative size");
-  if (B == 0) return PA_OK;
-  if (!out || !q || !block_tables || !context_lens) return fail(PA_EINVAL, "pa_decode: NULL argument");
-  if (H_q % pool->num_kv_heads) return fail(PA_EINVAL, "pa_decode: H_q must be a multiple of num_kv_heads");
-  if (static_cast<int64_t>(max_blocks) * pool->block_size < max_ctx)
-    return fail(PA_EINVAL, "pa_decode: max_blocks * block_size < max_ctx");
-  if (!aligned16(q) || !aligned16(pool->k) || !aligned16(pool->v))
-    return fail(PA_EINVAL, "pa_decode: q and pool must be 16-byte aligned");
-  if (B > 65535 || pool->num_kv_heads > 65535) return fail(PA_EINVAL, "pa_decode: grid too large");
-  const int G = H_q / pool->num_kv_heads;
-  DecodeFn fn = pick(pool->dtype, pool->head_dim, G, pool->block_size);
-  if (!fn) return fail(PA_ENOTSUP, "pa_decode: (dtype, head_dim, block_size, H_q/H_kv) not compiled");
-  DecodePlan pl = plan_decode(B, pool->num_kv_heads, G, pool->block_size, max_ctx);
-  const size_t need = workspace_bytes_for(pl, B, pool->num_kv_heads, H_q, pool->head_dim);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PA_ESPACE, "pa_decode: workspace of " + std::to_string(need) + " bytes needed");
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u))
-    return fail(PA_EINVAL, "pa_decode: workspace must be 4-byte aligned");
-  Workspace ws = carve(workspace, pl, B, pool->num_kv_heads, H_q);
-  const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  fn(pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens, scale_log2, pl, ws, stream);
-  return check_launch("pa_decode");
+  return pa::decode_entry("pa_decode", pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens, max_ctx,
+                          scale, workspace, workspace_bytes, pa::NewTokens{nullptr, nullptr, nullptr}, stream);
+}
+
+extern "C" int pa_decode_append(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, const void* k_new,
+                                const void* v_new, const int32_t* slot_mapping, int32_t B, int32_t H_q,
+                                const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                                int32_t max_ctx, float scale, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (B > 0 && (!k_new || !v_new || !slot_mapping)) return pa::fail(PA_EINVAL, "pa_decode_append: NULL new token input");
+  return pa::decode_entry("pa_decode_append", pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens,
+                          max_ctx, scale, workspace, workspace_bytes, pa::NewTokens{k_new, v_new, slot_mapping},
+                          stream);
 }

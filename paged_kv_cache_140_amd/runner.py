@@ -14,7 +14,7 @@ import torch
 from pa_inputs import gen
 
 from .api import (BlockManager, KVPool, OutOfBlocks, TORCH_DTYPE, decode_workspace, pa_cache_append,
-                  pa_copy_blocks, pa_decode, pa_prefill_chunk)
+                  pa_copy_blocks, pa_decode, pa_decode_append, pa_prefill_chunk)
 
 
 def to_device(x, dtype, device):
@@ -37,6 +37,9 @@ class StepInputs:
     workspace: object
     prefill: object = None  # (q, table, ctx_before, out)
     n_pairs: int = 0
+    # True when the step appends exactly one token to each decoded sequence,
+    # in decode order: then append + decode can run as one pa_decode_append.
+    fusable: bool = False
 
 
 class GpuRun:
@@ -120,6 +123,7 @@ class GpuRun:
             si.max_ctx = max_ctx
             si.out = torch.empty_like(si.q)
             si.workspace = decode_workspace(self.pool, len(step.decode_seqs), cfg["H_q"], max_ctx, dev)
+            si.fusable = list(step.appends) == [(s_, 1) for s_ in step.decode_seqs]
         if step.prefill is not None:
             pf = step.prefill
             table = np.array(self.bm.block_table(pf.seq), dtype=np.int32)
@@ -127,11 +131,17 @@ class GpuRun:
             si.prefill = (q, torch.from_numpy(table).to(dev), pf.ctx_before, torch.empty_like(q))
         return si
 
-    def launch(self, si, stream=None, do_copy=True, do_append=True, do_decode=True, do_prefill=True):
-        """Enqueue the step's kernels in the contract order: copies, appends, attention."""
+    def launch(self, si, stream=None, do_copy=True, do_append=True, do_decode=True, do_prefill=True, fused=False):
+        """Enqueue the step's kernels in the contract order: copies, appends,
+        attention.  ``fused``: a step that appends one token per decoded
+        sequence runs its append and decode as one pa_decode_append."""
         cfg = self.cfg
         if do_copy and si.n_pairs:
             pa_copy_blocks(self.pool, si.pairs, stream)
+        if fused and si.fusable and do_append and do_decode:
+            pa_decode_append(self.pool, self.layer, si.out, si.q, si.k_new, si.v_new, si.slots, si.tables, si.lens,
+                             si.max_ctx, cfg["scale"], si.workspace, stream)
+            do_append = do_decode = False
         if do_append and si.slots.numel():
             pa_cache_append(self.pool, self.layer, si.k_new, si.v_new, si.slots, stream)
         if do_decode and si.q is not None:
@@ -141,7 +151,7 @@ class GpuRun:
             q, table, ctx_before, out = si.prefill
             pa_prefill_chunk(self.pool, self.layer, out, q, table, ctx_before, cfg["scale"], stream)
 
-    def run_step(self, step):
+    def run_step(self, step, fused=False):
         si = self.prepare(step)
-        self.launch(si)
+        self.launch(si, fused=fused)
         return si

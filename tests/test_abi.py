@@ -21,7 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_hot_path():
     names = declared_functions()
-    for n in ("pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_prefill_chunk", "pa_decode_workspace_size",
+    for n in ("pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_append", "pa_prefill_chunk",
+              "pa_decode_workspace_size",
               "pa_status_string", "pa_bm_create", "pa_bm_append_slots", "pa_bm_fork", "pa_bm_free_seq"):
         assert n in names
 
@@ -68,6 +69,13 @@ def test_host_side_argument_checks_need_no_gpu():
     # max_blocks too small for max_ctx
     assert lib.pa_decode(ctypes.byref(pool), 0, 256, 256, 2, 16, 256, 2, 256, 100, 0.1, None, 0, None) == \
         _lib.PA_EINVAL
+    # fused append + decode: missing new-token inputs; misaligned k_new; B == 0
+    assert lib.pa_decode_append(ctypes.byref(pool), 0, 256, 256, None, 256, 256, 2, 16, 256, 64, 256, 100, 0.1,
+                                None, 0, None) == _lib.PA_EINVAL
+    assert lib.pa_decode_append(ctypes.byref(pool), 0, 256, 256, 264, 256, 256, 2, 16, 256, 64, 256, 100, 0.1,
+                                None, 0, None) == _lib.PA_EINVAL
+    assert lib.pa_decode_append(ctypes.byref(pool), 0, 256, 256, None, None, None, 0, 16, 256, 64, 256, 100, 0.1,
+                                None, 0, None) == _lib.PA_OK
     pool.head_dim = 96
     assert lib.pa_cache_append(ctypes.byref(pool), 0, 256, 256, 256, 4, None) == _lib.PA_ENOTSUP
     del args
