@@ -165,19 +165,23 @@ __global__ void __launch_bounds__(MAXT)
   const int j1 = min(j0 + blocks_per_part, nblk);
 
   // Fused append: this sequence's new token sits at position ctx - 1.  The
-  // partition holding that position masks that position out of its paged
-  // pass (vis = ctx - 1: the pool row may be read, stale, but never counts),
-  // and wave 0 adds the new token from the input at the end and writes it
-  // into its slot.  The unit walk itself stays that of a plain decode, so
-  // the first K/V loads do not wait for the slot.  A negative slot writes
-  // nothing and reads the pool's own row, as a plain decode would.
+  // partition holding that position processes the unit holding it last, as
+  // its masked tail, with that position masked out (vis = ctx - 1: the pool
+  // row may be read, stale, but never counts); wave 0 adds the new token from
+  // the input and writes it into its slot at the end.  Which unit is the
+  // tail depends on ctx only, so the first K/V loads do not wait for the
+  // slot, and the units streamed before it need no mask.  A negative slot
+  // writes nothing and lets the tail read the pool's own row, as a plain
+  // decode would.
   int vis = ctx;
+  bool holds_new = false;
   bool owns_new = false;
   int new_slot = -1;
   uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
   if constexpr (FUSED) {
+    holds_new = (ctx - 1) / BS >= j0 && (ctx - 1) / BS < j1;
     new_slot = __builtin_amdgcn_readfirstlane(new_slots[b]);
-    owns_new = new_slot >= 0 && (ctx - 1) / BS >= j0 && (ctx - 1) / BS < j1;
+    owns_new = holds_new && new_slot >= 0;
     const int64_t new_row = (static_cast<int64_t>(b) * gridDim.y + g) * D * S;  // [B][H_kv][D] inputs
     kx = load16(k_new + new_row + c * 16);  // every lane: a fixed number of loads keeps the waits exact
     vx = load16(v_new + new_row + c * 16);
@@ -317,13 +321,12 @@ __global__ void __launch_bounds__(MAXT)
     }
   };
 
-  // Units of this partition: full ones [u_first, u_full), stepping by W per
-  // wave, streamed through a ring of RING loads in flight; then at most one
-  // partly visible unit, handled by the wave that owns it.
+  // Units of this partition: unmasked ones [u_first, u_full), stepping by W
+  // per wave, streamed through a ring of RING loads in flight; then at most
+  // one masked unit (partly visible, or, fused, the one holding ctx - 1),
+  // handled by the wave that owns it.
   const int u_stop = min(j1 * UPB, (ctx + U - 1) / U);
-  const int u_full = min(u_stop, ctx / U);
-  // A full unit that holds the masked-out new token (fused, ctx % U == 0).
-  const int u_mask = FUSED && owns_new && ctx % U == 0 ? (ctx - 1) / U : -1;
+  const int u_full = FUSED && holds_new ? (ctx - 1) / U : min(u_stop, ctx / U);
   const int u_first = u_begin + wave;
   const int n_w = u_full > u_first ? (u_full - u_first + W - 1) / W : 0;  // this wave's full units
   // The partly visible last unit (if this partition has it) is loaded first,
@@ -354,7 +357,7 @@ __global__ void __launch_bounds__(MAXT)
         const int idx = k + p;
         if (idx < n_w) {
           const int u = u_first + idx * W;
-          process(u, kr[p], vr[p], FUSED && u == u_mask);
+          process(u, kr[p], vr[p], false);
         }
         // Keep refills in ring order: the in-order load counter then only
         // ever waits for the oldest slot.
