@@ -33,6 +33,7 @@
 
 #include <cmath>
 #include <cstdlib>
+#include <type_traits>
 
 #include "pa_common.h"
 
@@ -66,6 +67,26 @@ struct DecodeShape {
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A lane's value and that of lane ^ S, as a pair whose order differs
+// between lanes (callers combine the two symmetrically).  Lanes 16 and 32
+// apart: v_permlane16_swap / v_permlane32_swap; 8 apart: DPP row_ror:8.
+template <int S>
+__device__ __forceinline__ void pair_with(float x, float& a, float& b) {
+  static_assert(S == 8 || S == 16 || S == 32, "lane distance");
+  if constexpr (S == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    a = x;
+    b = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  }
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -333,23 +354,28 @@ __global__ void __launch_bounds__(MAXT)
   // by the wave it falls to, and processed last with masking.
   const bool has_tail = u_full < u_stop && u_full >= u_first && (u_full - u_first) % W == 0;
   uint4 kt[NLD], vt[NLD];
-  {
-    // Unconditional (a wave without the tail re-reads its partition's first
-    // unit, a cache hit): every wave then has the same loads in flight, and
-    // the waits below stay exact instead of draining the whole ring.
+  // The tail's table entry depends on ctx, one more dependent read than the
+  // ring's first entries: its loads go after the ring's so that they do not
+  // hold the ring's back.  Unconditional (a wave without the tail re-reads
+  // its partition's first unit, a cache hit): every wave then has the same
+  // loads in flight, and the waits below stay exact.
+  auto load_tail = [&]() __attribute__((always_inline)) {
     const int ut = has_tail ? u_full : u_begin;
     load_unit(ut, kt, vt, btrow[ut / UPB]);
-  }
+  };
   if (n_w > 0) {
     // Refills are unconditional, with the unit index clamped to the wave's
     // last one (a cache hit), so each ring slot stays in fixed registers and
-    // no load ever waits for a later one.
+    // no load ever waits for a later one.  A first-round slot past the
+    // wave's units re-reads its first unit, whose table entry is at hand.
     uint4 kr[RING][NLD], vr[RING][NLD];
 #pragma unroll
     for (int p = 0; p < RING; ++p) {
-      const int u = u_first + min(p, n_w - 1) * W;
-      load_unit(u, kr[p], vr[p], p < n_w ? ph[p] : btrow[u / UPB]);
+      const bool live = p < n_w;
+      load_unit(live ? u_first + p * W : u_first, kr[p], vr[p], live ? ph[p] : ph[0]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_tail();
     add_new_token();
     for (int k = 0; k < n_w; k += RING) {
 #pragma unroll
@@ -368,27 +394,39 @@ __global__ void __launch_bounds__(MAXT)
       }
     }
   }
-  if (n_w <= 0) add_new_token();
+  if (n_w <= 0) {
+    load_tail();
+    add_new_token();
+  }
   if (has_tail) process(u_full, kt, vt, true);
 
   // Merge the TPW row groups of this wave (lanes LPT, 2*LPT, ... apart hold
-  // the same dims of different tokens).
-#pragma unroll
-  for (int step = LPT; step < 64; step <<= 1) {
+  // the same dims of different tokens), with cross-lane VALU swaps.
+  static_assert(LPT >= 8, "row groups are at least 8 lanes wide");
+  auto merge_rows = [&](auto dist) __attribute__((always_inline)) {
+    constexpr int S = decltype(dist)::value;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], step);
-      const float lo = __shfl_xor(l[h], step);
-      const float mx = fmaxf(m[h], mo);
+      float m0, m1, l0, l1;
+      pair_with<S>(m[h], m0, m1);
+      pair_with<S>(l[h], l0, l1);
+      const float mx = fmaxf(m0, m1);
       const float ms = (mx == kNegInf) ? 0.0f : mx;
-      const float a = exp2_fast(m[h] - ms);
-      const float bo = exp2_fast(mo - ms);
-      l[h] = l[h] * a + lo * bo;
+      const float w0 = exp2_fast(m0 - ms);
+      const float w1 = exp2_fast(m1 - ms);
+      l[h] = l0 * w0 + l1 * w1;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] = acc[h][e] * a + __shfl_xor(acc[h][e], step) * bo;
+      for (int e = 0; e < VEC; ++e) {
+        float a0, a1;
+        pair_with<S>(acc[h][e], a0, a1);
+        acc[h][e] = a0 * w0 + a1 * w1;
+      }
       m[h] = mx;
     }
-  }
+  };
+  if constexpr (LPT <= 8) merge_rows(std::integral_constant<int, 8>{});
+  if constexpr (LPT <= 16) merge_rows(std::integral_constant<int, 16>{});
+  if constexpr (LPT <= 32) merge_rows(std::integral_constant<int, 32>{});
 
   // Waves -> LDS: sm_m[W][G], sm_l[W][G], sm_acc[W][G][D].
   float* sm_m = smem;
