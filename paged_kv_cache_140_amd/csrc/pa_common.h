@@ -92,6 +92,8 @@ constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8
 constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside each 16
+constexpr int kDppRor4 = 0x124;        // rotate by 4 lanes inside each 16
+constexpr int kDppRor8 = 0x128;        // lane i <-> i^8 inside each 16
 
 // Sum over aligned groups of N consecutive lanes (N = 2..64); every lane of
 // the group receives the group's sum.

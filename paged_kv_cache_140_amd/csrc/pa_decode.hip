@@ -41,10 +41,6 @@ namespace pa {
 
 constexpr float kNegInf = -INFINITY;
 
-#ifndef PA_DECODE_NT
-#define PA_DECODE_NT 0
-#endif
-
 // Unit = NLD wave loads of K and V (TPW tokens each), 2 units in flight per
 // wave.  Few query heads per KV head: short units.  Many heads (more
 // arithmetic per byte): longer units for more independent work per lane.
@@ -135,6 +131,58 @@ struct QChunk<F32> {
 };
 
 
+// Probabilities packed two tokens to a register in the pool's 16-bit type,
+// for P.V as packed dot products (exact products, fp32 accumulate).
+template <typename E>
+struct PPair;
+template <>
+struct PPair<BF16> {
+  static constexpr uint32_t kOnes = 0x3F803F80u;  // (1, 1)
+  __device__ static uint32_t pack(float a, float b) {
+    const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static float dot(uint32_t p, uint32_t v, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p), __builtin_bit_cast(bf16x2_t, v), c, false);
+  }
+};
+template <>
+struct PPair<F16> {
+  static constexpr uint32_t kOnes = 0x3C003C00u;  // (1, 1)
+  __device__ static uint32_t pack(float a, float b) {
+    const f16x2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static float dot(uint32_t p, uint32_t v, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p), __builtin_bit_cast(f16x2_t, v), c, false);
+  }
+};
+
+// Scattered heads: with G query heads per KV head, lane bits 5 and 4 pick a
+// quarter of the heads, so lane holds G/4 "own" heads: (G/2)*bit5 +
+// (G/4)*bit4 + j.  gather_heads turns the own heads' values into all G
+// heads' values, in head order, in every lane: v_permlane16_swap and
+// v_permlane32_swap of a register with itself return (the even row's value,
+// the odd row's value) and (the lower half's, the upper half's) in every
+// lane.
+template <int G>
+__device__ __forceinline__ void gather_heads(const uint32_t* own, uint32_t* all) {
+  constexpr int NH = G / 4;
+  uint32_t y[2 * NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    const auto t = __builtin_amdgcn_permlane16_swap(own[j], own[j], false, false);
+    y[j] = t[0];
+    y[j + NH] = t[1];
+  }
+#pragma unroll
+  for (int k = 0; k < 2 * NH; ++k) {
+    const auto t = __builtin_amdgcn_permlane32_swap(y[k], y[k], false, false);
+    all[k] = t[0];
+    all[k + 2 * NH] = t[1];
+  }
+}
+
 template <typename E, int D, int G, int BS, int MAXT, bool FUSED>
 __global__ void __launch_bounds__(MAXT)
     decode_kernel(char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off, int64_t head_stride,
@@ -157,8 +205,21 @@ __global__ void __launch_bounds__(MAXT)
   // so that a table read never waits on the vector loads in flight.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int r = lane / LPT;  // token row inside a wave load
-  const int c = lane % LPT;  // 16-byte chunk of the row
+  // Scattered-score layout (16-bit pools, G >= 4): lane bits 4 and 5 pick
+  // a quarter of a token row's 16-byte chunks, the CLO lowest bits a chunk
+  // inside it (a lane quad still reads 64 contiguous bytes), and the bits in
+  // between the token row.  q.k partial sums are then reduced across chunks
+  // by swaps 32 and 16 lanes apart that leave each lane the scores of G/4
+  // heads, so the softmax runs once per (token, head) per 4 lanes instead of
+  // once per lane of the row, and P.V takes packed dot products over token
+  // pairs.  Otherwise a row's chunks sit in adjacent lanes and every lane
+  // keeps all G heads' scores.
+  constexpr bool kScatter = S == 2 && G >= 4 && NLD % 2 == 0;
+  constexpr int NS = kScatter ? G / 4 : G;  // softmax states per lane
+  constexpr int CLO = LPT / 4;              // scattered layout: chunks in the low lane bits
+  static_assert(!kScatter || TPW == 4 || TPW == 8, "scattered layout: 4 or 8 token rows");
+  const int r = kScatter ? (lane / CLO) % TPW : lane / LPT;            // token row inside a wave load
+  const int c = kScatter ? lane % CLO + CLO * (lane / 16) : lane % LPT;  // 16-byte chunk of the row
 
   const int j0 = part * blocks_per_part;
   const int u_begin = j0 * UPB;
@@ -213,11 +274,14 @@ __global__ void __launch_bounds__(MAXT)
 #pragma unroll
   for (int h = 0; h < G; ++h) qc[h].set(load16(q + ((head0 + h) * D + c * VEC) * S));
 
-  float m[G], l[G], acc[G][VEC];
+  float m[NS], l[NS], acc[G][VEC];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    m[j] = kNegInf;
+    l[j] = 0.0f;
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.0f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[h][e] = 0.0f;
   }
@@ -231,26 +295,108 @@ __global__ void __launch_bounds__(MAXT)
     const int64_t off = (phys * BS + (u % UPB) * U) * static_cast<int64_t>(D * S) + lane_off;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-#if PA_DECODE_NT
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off + i * TPW * D * S));
-      const u32x4 bb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off + i * TPW * D * S));
-      kr[i] = make_uint4(a.x, a.y, a.z, a.w);
-      vr[i] = make_uint4(bb.x, bb.y, bb.z, bb.w);
-#else
       kr[i] = load16(kbase + off + i * TPW * D * S);
       vr[i] = load16(vbase + off + i * TPW * D * S);
-#endif
     }
   };
 
-  // One unit: NLD tokens per lane row, online-softmax update for G heads.
-  auto process = [&](int u, const uint4* kr, const uint4* vr, bool masked) {
+  // One unit: NLD tokens per lane row, online-softmax update for G heads;
+  // with ``masked``, tokens at positions >= vis_ take no part.
+  auto process = [&](int u, const uint4* kr, const uint4* vr, bool masked, int vis_) {
     const int tok0 = u * U + r;
+    if constexpr (kScatter) {
+      constexpr int NH = G / 4;
+      float x[NLD][NH];
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        float sp[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) sp[h] = qc[h].dot(kr[i]);
+        // Chunks 32 lanes apart: the lower half keeps heads [0, G/2), the
+        // upper half [G/2, G); then 16 apart: a quarter each.
+        float w[G / 2];
+#pragma unroll
+        for (int h = 0; h < G / 2; ++h) {
+          const auto t =
+              __builtin_amdgcn_permlane32_swap(__float_as_uint(sp[h]), __float_as_uint(sp[h + G / 2]), false, false);
+          w[h] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+        }
+        const bool dead = masked && tok0 + i * TPW >= vis_;
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const auto t =
+              __builtin_amdgcn_permlane16_swap(__float_as_uint(w[j]), __float_as_uint(w[j + NH]), false, false);
+          float y = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+          // the remaining chunk bits: the lowest lane bits
+          y += dpp_move<kDppXor1>(y);
+          if constexpr (CLO == 4) y += dpp_move<kDppXor2>(y);
+          x[i][j] = dead ? kNegInf : y * scale_log2;
+        }
+      }
+      float mx[NH];
+      bool grew = false;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        mx[j] = m[j];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) mx[j] = fmaxf(mx[j], x[i][j]);
+        grew |= mx[j] > m[j];
+      }
+      if (__any(grew)) {
+        uint32_t al[NH], alg[G];
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const float alpha = exp2_fast(m[j] - ((mx[j] == kNegInf) ? 0.0f : mx[j]));
+          m[j] = mx[j];
+          l[j] *= alpha;
+          al[j] = __float_as_uint(alpha);
+        }
+        gather_heads<G>(al, alg);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[h][e] *= __uint_as_float(alg[h]);
+        }
+      }
+      float msafe[NH];
+#pragma unroll
+      for (int j = 0; j < NH; ++j) msafe[j] = (m[j] == kNegInf) ? 0.0f : m[j];
+#pragma unroll
+      for (int q2 = 0; q2 < NLD / 2; ++q2) {
+        // Tokens 2*q2 and 2*q2+1 of the lane: probabilities packed per own
+        // head (l sums the packed values, so it weighs what P.V weighs),
+        // then gathered for all heads.
+        uint32_t pk[NH], pg[G];
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          pk[j] = PPair<E>::pack(exp2_fast(x[2 * q2][j] - msafe[j]), exp2_fast(x[2 * q2 + 1][j] - msafe[j]));
+          l[j] = PPair<E>::dot(pk[j], PPair<E>::kOnes, l[j]);
+        }
+        gather_heads<G>(pk, pg);
+        uint4 va = vr[2 * q2], vb = vr[2 * q2 + 1];
+        // unused slots may hold anything (NaN included): select, not multiply
+        if (masked && tok0 + 2 * q2 * TPW >= vis_) va = make_uint4(0, 0, 0, 0);
+        if (masked && tok0 + (2 * q2 + 1) * TPW >= vis_) vb = make_uint4(0, 0, 0, 0);
+        const uint32_t a4[4] = {va.x, va.y, va.z, va.w};
+        const uint32_t b4[4] = {vb.x, vb.y, vb.z, vb.w};
+        uint32_t vp[VEC];  // (element e of token 2*q2, element e of token 2*q2+1)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          vp[2 * d] = __builtin_amdgcn_perm(b4[d], a4[d], 0x05040100u);
+          vp[2 * d + 1] = __builtin_amdgcn_perm(b4[d], a4[d], 0x07060302u);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[h][e] = PPair<E>::dot(pg[h], vp[e], acc[h][e]);
+        }
+      }
+      return;
+    }
     float s[NLD][G];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const bool dead = masked && tok0 + i * TPW >= vis;
+      const bool dead = masked && tok0 + i * TPW >= vis_;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float d = group_sum<LPT>(qc[h].dot(kr[i])) * scale_log2;
@@ -285,7 +431,7 @@ __global__ void __launch_bounds__(MAXT)
     for (int i = 0; i < NLD; ++i) {
       float vf[VEC];
       widen(E{}, vr[i], vf);
-      if (masked && tok0 + i * TPW >= vis) {
+      if (masked && tok0 + i * TPW >= vis_) {
         // unused slots may hold anything (NaN included): select, not multiply
 #pragma unroll
         for (int e = 0; e < VEC; ++e) vf[e] = 0.0f;
@@ -302,42 +448,15 @@ __global__ void __launch_bounds__(MAXT)
 
   // Fused: the new token's share of the attention, added by wave 0 of the
   // partition that holds it, right after the wave's first K/V loads are in
-  // flight (so its own input load overlaps them).  Row 0 of the wave's lane
-  // rows holds it; the other rows take no part (score -inf, value 0).
+  // flight (so its own input load overlaps them): a unit whose only live
+  // token is row 0 of its first load, taken from the input.
   auto add_new_token = [&]() {
     if constexpr (FUSED) {
       if (owns_new && wave == 0) {
-        float sx[G];
+        uint4 kxa[NLD], vxa[NLD];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float d = group_sum<LPT>(qc[h].dot(kx)) * scale_log2;
-          sx[h] = r == 0 ? d : kNegInf;
-        }
-        bool grew = false;
-#pragma unroll
-        for (int h = 0; h < G; ++h) grew |= sx[h] > m[h];
-        if (__any(grew)) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float mx = fmaxf(m[h], sx[h]);
-            const float alpha = exp2_fast(m[h] - ((mx == kNegInf) ? 0.0f : mx));
-            m[h] = mx;
-            l[h] *= alpha;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
-          }
-        }
-        float vf[VEC];
-        widen(E{}, vx, vf);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) vf[e] = r == 0 ? vf[e] : 0.0f;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = exp2_fast(sx[h] - ((m[h] == kNegInf) ? 0.0f : m[h]));
-          l[h] += p;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
-        }
+        for (int i = 0; i < NLD; ++i) kxa[i] = kx, vxa[i] = vx;
+        process(0, kxa, vxa, true, 1);
       }
     }
   };
@@ -383,7 +502,7 @@ __global__ void __launch_bounds__(MAXT)
         const int idx = k + p;
         if (idx < n_w) {
           const int u = u_first + idx * W;
-          process(u, kr[p], vr[p], false);
+          process(u, kr[p], vr[p], false, vis);
         }
         // Keep refills in ring order: the in-order load counter then only
         // ever waits for the oldest slot.
@@ -398,41 +517,75 @@ __global__ void __launch_bounds__(MAXT)
     load_tail();
     add_new_token();
   }
-  if (has_tail) process(u_full, kt, vt, true);
+  if (has_tail) process(u_full, kt, vt, true, vis);
 
-  // Merge the TPW row groups of this wave (lanes LPT, 2*LPT, ... apart hold
-  // the same dims of different tokens), with cross-lane VALU swaps.
-  static_assert(LPT >= 8, "row groups are at least 8 lanes wide");
-  auto merge_rows = [&](auto dist) __attribute__((always_inline)) {
-    constexpr int S = decltype(dist)::value;
+  // Softmax state of all G heads in every lane: mg, lg.
+  float mg[G], lg[G];
+  if constexpr (kScatter) {
+    uint32_t mo[NS], lo[NS], ma[G], la[G];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) mo[j] = __float_as_uint(m[j]), lo[j] = __float_as_uint(l[j]);
+    gather_heads<G>(mo, ma);
+    gather_heads<G>(lo, la);
+#pragma unroll
+    for (int h = 0; h < G; ++h) mg[h] = __uint_as_float(ma[h]), lg[h] = __uint_as_float(la[h]);
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) mg[h] = m[h], lg[h] = l[h];
+  }
+
+  // Merge the TPW row groups of this wave (lanes holding the same dims of
+  // different tokens) with cross-lane VALU moves: pair_with gives a lane its
+  // own value and its partner's, in either order, and the combine is
+  // symmetric in the two.
+  auto combine = [&](auto pair) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float m0, m1, l0, l1;
-      pair_with<S>(m[h], m0, m1);
-      pair_with<S>(l[h], l0, l1);
+      pair(mg[h], m0, m1);
+      pair(lg[h], l0, l1);
       const float mx = fmaxf(m0, m1);
       const float ms = (mx == kNegInf) ? 0.0f : mx;
       const float w0 = exp2_fast(m0 - ms);
       const float w1 = exp2_fast(m1 - ms);
-      l[h] = l0 * w0 + l1 * w1;
+      lg[h] = l0 * w0 + l1 * w1;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         float a0, a1;
-        pair_with<S>(acc[h][e], a0, a1);
+        pair(acc[h][e], a0, a1);
         acc[h][e] = a0 * w0 + a1 * w1;
       }
-      m[h] = mx;
+      mg[h] = mx;
     }
   };
-  if constexpr (LPT <= 8) merge_rows(std::integral_constant<int, 8>{});
-  if constexpr (LPT <= 16) merge_rows(std::integral_constant<int, 16>{});
-  if constexpr (LPT <= 32) merge_rows(std::integral_constant<int, 32>{});
+  auto dpp_pair = [](auto ctl) {
+    return [](float x, float& a, float& b) __attribute__((always_inline)) {
+      a = x;
+      b = dpp_move<decltype(ctl)::value>(x);
+    };
+  };
+  auto swap_pair = [](auto dist) {
+    return [](float x, float& a, float& b) __attribute__((always_inline)) { pair_with<decltype(dist)::value>(x, a, b); };
+  };
+  if constexpr (kScatter) {
+    // rows in lane bits log2(CLO)..3: lane 2 apart (8 rows), then rotations
+    // by 4 and 8 inside each 16, which reach all rows of bits 2 and 3
+    if constexpr (CLO == 2) combine(dpp_pair(std::integral_constant<int, kDppXor2>{}));
+    combine(dpp_pair(std::integral_constant<int, kDppRor4>{}));
+    combine(dpp_pair(std::integral_constant<int, kDppRor8>{}));
+  } else {
+    // rows in lane bits log2(LPT)..5
+    static_assert(LPT >= 8, "row groups are at least 8 lanes wide");
+    if constexpr (LPT <= 8) combine(swap_pair(std::integral_constant<int, 8>{}));
+    if constexpr (LPT <= 16) combine(swap_pair(std::integral_constant<int, 16>{}));
+    if constexpr (LPT <= 32) combine(swap_pair(std::integral_constant<int, 32>{}));
+  }
 
   // Waves -> LDS: sm_m[W][G], sm_l[W][G], sm_acc[W][G][D].
   float* sm_m = smem;
   float* sm_l = smem + W * G;
   float* sm_acc = smem + 2 * W * G;
-  if (lane < LPT) {
+  if (r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -442,8 +595,8 @@ __global__ void __launch_bounds__(MAXT)
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      sm_m[wave * G + h] = m[h];
-      sm_l[wave * G + h] = l[h];
+      sm_m[wave * G + h] = mg[h];
+      sm_l[wave * G + h] = lg[h];
     }
   }
   __syncthreads();
