@@ -158,28 +158,34 @@ struct PPair<F16> {
   }
 };
 
-// Scattered heads: with G query heads per KV head, lane bits 5 and 4 pick a
-// quarter of the heads, so lane holds G/4 "own" heads: (G/2)*bit5 +
-// (G/4)*bit4 + j.  gather_heads turns the own heads' values into all G
-// heads' values, in head order, in every lane: v_permlane16_swap and
-// v_permlane32_swap of a register with itself return (the even row's value,
-// the odd row's value) and (the lower half's, the upper half's) in every
-// lane.
+// Scattered heads: with G >= 4 query heads per KV head, lane bits 5 and 4
+// pick a quarter of the heads, so a lane holds G/4 "own" heads: (G/2)*bit5 +
+// (G/4)*bit4 + j; with G = 2, bit 5 picks the lane's one head.  gather_heads
+// turns the own heads' values into all G heads' values, in head order, in
+// every lane: v_permlane16_swap and v_permlane32_swap of a register with
+// itself return (the even row's value, the odd row's value) and (the lower
+// half's, the upper half's) in every lane.
 template <int G>
 __device__ __forceinline__ void gather_heads(const uint32_t* own, uint32_t* all) {
-  constexpr int NH = G / 4;
-  uint32_t y[2 * NH];
+  if constexpr (G == 2) {
+    const auto t = __builtin_amdgcn_permlane32_swap(own[0], own[0], false, false);
+    all[0] = t[0];
+    all[1] = t[1];
+  } else {
+    constexpr int NH = G / 4;
+    uint32_t y[2 * NH];
 #pragma unroll
-  for (int j = 0; j < NH; ++j) {
-    const auto t = __builtin_amdgcn_permlane16_swap(own[j], own[j], false, false);
-    y[j] = t[0];
-    y[j + NH] = t[1];
-  }
+    for (int j = 0; j < NH; ++j) {
+      const auto t = __builtin_amdgcn_permlane16_swap(own[j], own[j], false, false);
+      y[j] = t[0];
+      y[j + NH] = t[1];
+    }
 #pragma unroll
-  for (int k = 0; k < 2 * NH; ++k) {
-    const auto t = __builtin_amdgcn_permlane32_swap(y[k], y[k], false, false);
-    all[k] = t[0];
-    all[k + 2 * NH] = t[1];
+    for (int k = 0; k < 2 * NH; ++k) {
+      const auto t = __builtin_amdgcn_permlane32_swap(y[k], y[k], false, false);
+      all[k] = t[0];
+      all[k + 2 * NH] = t[1];
+    }
   }
 }
 
@@ -214,8 +220,8 @@ __global__ void __launch_bounds__(MAXT)
   // once per lane of the row, and P.V takes packed dot products over token
   // pairs.  Otherwise a row's chunks sit in adjacent lanes and every lane
   // keeps all G heads' scores.
-  constexpr bool kScatter = S == 2 && G >= 4 && NLD % 2 == 0;
-  constexpr int NS = kScatter ? G / 4 : G;  // softmax states per lane
+  constexpr bool kScatter = S == 2 && G >= 2 && NLD % 2 == 0;
+  constexpr int NS = kScatter ? (G >= 4 ? G / 4 : 1) : G;  // softmax states per lane
   constexpr int CLO = LPT / 4;              // scattered layout: chunks in the low lane bits
   static_assert(!kScatter || TPW == 4 || TPW == 8, "scattered layout: 4 or 8 token rows");
   const int r = kScatter ? (lane / CLO) % TPW : lane / LPT;            // token row inside a wave load
@@ -305,7 +311,7 @@ __global__ void __launch_bounds__(MAXT)
   auto process = [&](int u, const uint4* kr, const uint4* vr, bool masked, int vis_) {
     const int tok0 = u * U + r;
     if constexpr (kScatter) {
-      constexpr int NH = G / 4;
+      constexpr int NH = NS;
       float x[NLD][NH];
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
@@ -324,8 +330,15 @@ __global__ void __launch_bounds__(MAXT)
         const bool dead = masked && tok0 + i * TPW >= vis_;
 #pragma unroll
         for (int j = 0; j < NH; ++j) {
-          const auto t =
-              __builtin_amdgcn_permlane16_swap(__float_as_uint(w[j]), __float_as_uint(w[j + NH]), false, false);
+          // G >= 4: chunks 16 lanes apart split the heads again; G = 2: they
+          // are summed (each lane keeps its one head).
+          uint32_t w2;
+          if constexpr (G >= 4) {
+            w2 = __float_as_uint(w[j + NH]);
+          } else {
+            w2 = __float_as_uint(w[j]);
+          }
+          const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[j]), w2, false, false);
           float y = __uint_as_float(t[0]) + __uint_as_float(t[1]);
           // the remaining chunk bits: the lowest lane bits
           y += dpp_move<kDppXor1>(y);
