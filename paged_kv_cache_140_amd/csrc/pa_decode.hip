@@ -10,7 +10,7 @@
 //
 // How, on CDNA4 (bandwidth-bound: 2*G flops per K/V element read, G = query
 // heads per KV head; no matrix cores):
-//  * grid (partition, kv head, sequence).  A partition is a run of blocks of
+//  * grid (kv head, partition, sequence).  A partition is a run of blocks of
 //    one sequence; one K/V read serves all G query heads of the KV head.
 //  * inside a workgroup each wave takes every W-th unit of U tokens
 //    (U <= block size) and keeps the next unit's K and V in flight in
@@ -202,8 +202,15 @@ __global__ void __launch_bounds__(MAXT)
                 RING = Sh::RING;
   extern __shared__ float smem[];
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
+  // Grid (kv head, partition, sequence), kv head fastest: workgroup i runs on
+  // XCD i % 8, so with H_kv a multiple of 8 every XCD gets the same heads of
+  // every partition of every sequence -- the same bytes.  With the partition
+  // fastest, a partition count that is a multiple of 8 would put every
+  // sequence's first partition (always present) on one XCD and the late ones
+  // (long sequences only) on another.
+  const int g = blockIdx.x;
+  const int part = blockIdx.y;
+  const int H_kv = gridDim.x;
   const int b = blockIdx.z;
   const int W = blockDim.x >> 6;
   // Wave-uniform by construction; readfirstlane lets the compiler keep the
@@ -270,7 +277,7 @@ __global__ void __launch_bounds__(MAXT)
     holds_new = (ctx - 1) / BS >= j0 && (ctx - 1) / BS < j1;
     new_slot = __builtin_amdgcn_readfirstlane(new_slots[b]);
     owns_new = holds_new && new_slot >= 0;
-    const int64_t new_row = (static_cast<int64_t>(b) * gridDim.y + g) * D * S;  // [B][H_kv][D] inputs
+    const int64_t new_row = (static_cast<int64_t>(b) * H_kv + g) * D * S;  // [B][H_kv][D] inputs
     kx = load16(k_new + new_row + c * 16);  // every lane: a fixed number of loads keeps the waits exact
     vx = load16(v_new + new_row + c * 16);
     if (owns_new) vis = ctx - 1;
@@ -788,7 +795,7 @@ static void launch_decode(const pa_kv_pool* pool, int32_t layer, void* out, cons
   const int64_t head_stride = static_cast<int64_t>(pool->num_blocks) * BS * D * E::bytes;
   const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * head_stride;
   const size_t lds = static_cast<size_t>(pl.waves) * G * (D + 2) * sizeof(float);
-  dim3 grid(pl.num_parts, pool->num_kv_heads, B);
+  dim3 grid(pool->num_kv_heads, pl.num_parts, B);
   hipLaunchKernelGGL((decode_kernel<E, D, G, BS, max_threads<G>(), FUSED>), grid, dim3(64 * pl.waves), lds, stream,
                      static_cast<char*>(pool->k), static_cast<char*>(pool->v), layer_off, head_stride,
                      static_cast<const char*>(q), out, bt, max_blocks, ctx, scale_log2, H_q, pl.blocks_per_part,
@@ -878,6 +885,7 @@ static int decode_entry(const char* who, const pa_kv_pool* pool, int32_t layer, 
   DecodeFn fn = pick(pool->dtype, pool->head_dim, G, pool->block_size, nt.slots != nullptr);
   if (!fn) return fail(PA_ENOTSUP, w + ": (dtype, head_dim, block_size, H_q/H_kv) not compiled");
   DecodePlan pl = plan_decode(B, pool->num_kv_heads, G, pool->block_size, max_ctx);
+  if (pl.num_parts > 65535) return fail(PA_EINVAL, w + ": too many partitions for the grid");
   const size_t need = workspace_bytes_for(pl, B, pool->num_kv_heads, H_q, pool->head_dim);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_ESPACE, w + ": workspace of " + std::to_string(need) + " bytes needed");
