@@ -34,7 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # WRITE_SIZE passes, calibrated against a plain copy of known size).  Used only
 # while the kernel sources still hash to the value recorded with the counters.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b32_gqa16x8_ctx512-640_traffic.json")
-DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_140_amd", "csrc", f) for f in ("pa_decode.hip", "pa_common.h")]
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_140_amd", "csrc", f)
+                  for f in ("pa_decode.hip", "pa_decode_dev.h", "pa_common.h")]
+HEADLINE_KERNEL = "pa::decode_kernel<pa::BF16, 128, 2, 16, 1024, true>"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def sources_sha256(paths):
@@ -59,6 +62,65 @@ def recorded_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
+def write_traffic_record(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
+    """Turn two rocprofv3 counter runs of this script (``--pmc FETCH_SIZE``,
+    then ``--pmc WRITE_SIZE``, each ``-f csv``) into the traffic record that
+    ``roofline.traffic`` reports.  Each counter is summed over its instances
+    per dispatch and scaled by what it reads for the 512 MiB plain copy that
+    this script runs first (true size known)."""
+    import csv
+    import glob
+    import statistics
+
+    def per_dispatch(d, counter):
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        acc, names = {}, {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = int(r["Dispatch_Id"])
+                acc[k] = acc.get(k, 0.0) + float(r["Counter_Value"])
+                names[k] = r["Kernel_Name"]
+        return acc, names
+
+    fetch, fnames = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, wnames = per_dispatch(write_dir, "WRITE_SIZE")
+    copy_kib = (512 << 20) / 1024
+    f_copy = max(v for k, v in fetch.items() if COPY_KERNEL in fnames[k])
+    w_copy = max(v for k, v in write.items() if COPY_KERNEL in wnames[k])
+    f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
+    f_head = statistics.median(v for k, v in fetch.items() if HEADLINE_KERNEL + "(" in fnames[k])
+    w_head = statistics.median(v for k, v in write.items() if HEADLINE_KERNEL + "(" in wnames[k])
+    n = sum(1 for k in fetch if HEADLINE_KERNEL + "(" in fnames[k])
+    traffic = int(round((f_head * f_scale + w_head * w_scale) * 1024))
+    algorithmic = 75289232
+    rec = {
+        "kernel": HEADLINE_KERNEL + " (pa_decode_append: append + decode)",
+        "workload": "B=32, GQA 16/8, head_dim 128, block 16, ctx U[512,640]+1, seed 0, 28 layers rotated; one new "
+                    "token per sequence appended in the same launch",
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -- python bench.py --no-cpu-baseline --no-rows",
+            "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -- python bench.py --no-cpu-baseline --no-rows",
+            "python bench.py --traffic-record gpurun_out/prof_fetch gpurun_out/prof_write",
+        ],
+        "dispatches": n,
+        "fetch_size_kib_per_dispatch_median": f_head,
+        "write_size_kib_per_dispatch_median": w_head,
+        "calibration": {"kernel": COPY_KERNEL + " (torch copy of 512 MiB, run first by bench.py)",
+                        "fetch_size_kib": f_copy, "write_size_kib": w_copy, "true_kib": copy_kib,
+                        "fetch_scale": f_scale, "write_scale": w_scale},
+        "traffic_bytes_per_launch": traffic,
+        "algorithmic_bytes_per_launch": algorithmic,
+        "traffic_over_algorithmic": round(traffic / algorithmic, 4),
+        "source_sha256": sources_sha256(DECODE_SOURCES),
+        "sources": [os.path.relpath(p, ROOT) for p in DECODE_SOURCES],
+    }
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -70,6 +132,8 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="skip the other workloads' rows")
     ap.add_argument("--copy-calibration-mib", type=int, default=512,
                     help="size of a plain device copy run once before timing (counter calibration)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the decode traffic record from two rocprofv3 counter runs, then exit (no GPU)")
     return ap.parse_args()
 
 
@@ -129,6 +193,9 @@ def time_loop(torch, fn, iters, warmup, replays=5):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        write_traffic_record(*args.traffic_record)
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the hot path is measured on one GPU's share; "
@@ -299,6 +366,14 @@ def main():
                                  "ms": round(ms_p5, 5),
                                  "TFLOPs": round(fl / (ms_p5 * 1e-3) / 1e12, 1),
                                  "mfma_frac": round(fl / (ms_p5 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+        ms_sep = time_loop(torch, lambda i: g5.launch(s5, do_copy=False, do_append=False), 10, 2)
+        ms_mix = time_loop(torch, lambda i: g5.launch(s5, do_copy=False, do_append=False, mixed=True), 10, 2)
+        rows["mixed_batch"] = {"workload": "the 63 decodes and the 1,024-token chunk as one pa_mixed_batch launch "
+                                           "(+ the partition merge), against pa_decode + pa_prefill_chunk",
+                               "ms": round(ms_mix, 5), "separate_ms": round(ms_sep, 5),
+                               "speedup": round(ms_sep / ms_mix, 3),
+                               "GBps": round(decode_bytes(L5, 8, 64, 128, 16, 2) / (ms_mix * 1e-3) / 1e9, 1),
+                               "TFLOPs": round(fl / (ms_mix * 1e-3) / 1e12, 1)}
         del g5, s5
         torch.cuda.empty_cache()
         out["rows"] = rows

@@ -16,5 +16,6 @@ from .api import (  # noqa: F401
     pa_decode,
     pa_decode_append,
     pa_decode_workspace_size,
+    pa_mixed_batch,
     pa_prefill_chunk,
 )

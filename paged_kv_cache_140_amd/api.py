@@ -147,6 +147,36 @@ def pa_prefill_chunk(pool, layer, out, q, block_table, ctx_before, scale, stream
           "pa_prefill_chunk")
 
 
+def pa_mixed_batch(pool, layer, dec_out, dec_q, block_tables, context_lens, max_ctx, pf_out, pf_q, pf_table,
+                   ctx_before, scale, prefill_workgroups=0, workspace=None, stream=None):
+    """A decode batch (as pa_decode) and one prefill chunk (as
+    pa_prefill_chunk) in one launch.  dec_q may have B = 0 rows and pf_q
+    T = 0 rows."""
+    B, H_q, _ = (int(x) for x in dec_q.shape)
+    T = int(pf_q.shape[0])
+    _need(dec_q, "dec_q", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(dec_out, "dec_out", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B][max_blocks]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    _need(pf_q, "pf_q", pool.torch_dtype, (T, H_q, pool.head_dim))
+    _need(pf_out, "pf_out", pool.torch_dtype, (T, H_q, pool.head_dim))
+    _need(pf_table, "pf_table", torch.int32)
+    if pf_table.dim() != 1:
+        raise ValueError("pf_table must be 1-D")
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    s = pool.struct()
+    check(lib().pa_mixed_batch(ctypes.byref(s), layer, _ptr(dec_out), _ptr(dec_q), B, H_q, _ptr(block_tables),
+                               int(block_tables.shape[1]), _ptr(context_lens), int(max_ctx), _ptr(pf_out),
+                               _ptr(pf_q), T, _ptr(pf_table), int(pf_table.shape[0]), int(ctx_before), float(scale),
+                               int(prefill_workgroups), _ptr(workspace), ws_bytes, _stream(stream)),
+          "pa_mixed_batch")
+
+
 def decode_workspace(pool, B, H_q, max_ctx, device="cuda"):
     """A workspace tensor of the size pa_decode needs (None if it needs none)."""
     n = pa_decode_workspace_size(pool, B, H_q, max_ctx)

@@ -19,4 +19,45 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Validates the pool struct and the layer index.
 int check_pool(const pa_kv_pool* pool, int32_t layer);
 
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Integer environment variable (tuning overrides), or dflt.
+int env_int(const char* name, int dflt);
+
+// ---------------------------------------------------------------- decode
+// Grid plan of a decode from host-side sizes only (context lengths stay on
+// the device): waves per workgroup, and the split of each sequence into
+// partitions of blocks_per_part blocks (num_parts of them for max_ctx).
+struct DecodePlan {
+  int waves;
+  int blocks_per_part;
+  int num_parts;
+};
+DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx);
+
+// Workspace of a split decode: (m, l) partials [B][H_q][P][2], then the
+// un-normalised weighted V sums [B][H_q][P][D], fp32.
+struct Workspace {
+  float* ml;
+  float* acc;
+};
+size_t workspace_bytes_for(const DecodePlan& pl, int B, int H_kv, int H_q, int D);
+Workspace carve(void* ws, const DecodePlan& pl, int B, int H_kv, int H_q);
+
+// Host-side checks of a decode call's arguments (PA_OK for B == 0).
+int validate_decode(const std::string& who, const pa_kv_pool* pool, int32_t layer, void* out, const void* q,
+                    int32_t B, int32_t H_q, const int32_t* block_tables, int32_t max_blocks,
+                    const int32_t* context_lens, int32_t max_ctx);
+// Checks the caller's workspace against the plan and carves it.
+int decode_workspace_check(const std::string& who, const DecodePlan& pl, const pa_kv_pool* pool, int32_t B,
+                           int32_t H_q, void* workspace, size_t workspace_bytes, Workspace* ws);
+// Enqueues the kernel that merges the partitions of a split decode.
+void launch_decode_merge(int dtype, int D, void* out, const Workspace& ws, const int32_t* ctx, int32_t B,
+                         int32_t H_q, const DecodePlan& pl, int bs, hipStream_t stream);
+
+// ---------------------------------------------------------------- prefill
+// Host-side checks of a prefill chunk's arguments (PA_OK for T == 0).
+int validate_prefill(const std::string& who, const pa_kv_pool* pool, int32_t layer, void* out, const void* q,
+                     int32_t T, int32_t H_q, const int32_t* block_table, int32_t nb, int32_t ctx_before);
+
 }  // namespace pa

@@ -14,7 +14,7 @@ import torch
 from pa_inputs import gen
 
 from .api import (BlockManager, KVPool, OutOfBlocks, TORCH_DTYPE, decode_workspace, pa_cache_append,
-                  pa_copy_blocks, pa_decode, pa_decode_append, pa_prefill_chunk)
+                  pa_copy_blocks, pa_decode, pa_decode_append, pa_mixed_batch, pa_prefill_chunk)
 
 
 def to_device(x, dtype, device):
@@ -131,11 +131,23 @@ class GpuRun:
             si.prefill = (q, torch.from_numpy(table).to(dev), pf.ctx_before, torch.empty_like(q))
         return si
 
-    def launch(self, si, stream=None, do_copy=True, do_append=True, do_decode=True, do_prefill=True, fused=False):
+    def launch(self, si, stream=None, do_copy=True, do_append=True, do_decode=True, do_prefill=True, fused=False,
+               mixed=False, prefill_workgroups=0):
         """Enqueue the step's kernels in the contract order: copies, appends,
         attention.  ``fused``: a step that appends one token per decoded
-        sequence runs its append and decode as one pa_decode_append."""
+        sequence runs its append and decode as one pa_decode_append.
+        ``mixed``: a step with both a decode batch and a prefill chunk runs
+        the two attentions as one pa_mixed_batch."""
         cfg = self.cfg
+        if mixed and do_decode and do_prefill and si.q is not None and si.prefill is not None:
+            if do_copy and si.n_pairs:
+                pa_copy_blocks(self.pool, si.pairs, stream)
+            if do_append and si.slots.numel():
+                pa_cache_append(self.pool, self.layer, si.k_new, si.v_new, si.slots, stream)
+            q, table, ctx_before, out = si.prefill
+            pa_mixed_batch(self.pool, self.layer, si.out, si.q, si.tables, si.lens, si.max_ctx, out, q, table,
+                           ctx_before, cfg["scale"], prefill_workgroups, si.workspace, stream)
+            return
         if do_copy and si.n_pairs:
             pa_copy_blocks(self.pool, si.pairs, stream)
         if fused and si.fusable and do_append and do_decode:

@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_hot_path():
     names = declared_functions()
     for n in ("pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_append", "pa_prefill_chunk",
-              "pa_decode_workspace_size",
+              "pa_mixed_batch", "pa_decode_workspace_size",
               "pa_status_string", "pa_bm_create", "pa_bm_append_slots", "pa_bm_fork", "pa_bm_free_seq"):
         assert n in names
 
@@ -76,6 +76,18 @@ def test_host_side_argument_checks_need_no_gpu():
                                 None, 0, None) == _lib.PA_EINVAL
     assert lib.pa_decode_append(ctypes.byref(pool), 0, 256, 256, None, None, None, 0, 16, 256, 64, 256, 100, 0.1,
                                 None, 0, None) == _lib.PA_OK
+    # mixed batch: both halves empty; H_q not a multiple of H_kv; chunk table too short; negative
+    # prefill workgroups; an f32 pool (no matrix-core path)
+    def mixed(B, H_q, T, nb=8, n_pre=0):
+        return lib.pa_mixed_batch(ctypes.byref(pool), 0, 256, 256, B, H_q, 256, 64, 256, 100, 256, 256, T, 256, nb,
+                                  100, 0.1, n_pre, None, 0, None)
+    assert mixed(0, 16, 0) == _lib.PA_OK
+    assert mixed(2, 12, 0) == _lib.PA_EINVAL
+    assert mixed(0, 16, 100, nb=12) == _lib.PA_EINVAL  # (100 + 100) / 16 -> 13 blocks needed
+    assert mixed(0, 16, 100, nb=13, n_pre=-1) == _lib.PA_EINVAL
+    pool.dtype = _lib.PA_F32
+    assert mixed(2, 16, 0) == _lib.PA_ENOTSUP
+    pool.dtype = _lib.PA_BF16
     pool.head_dim = 96
     assert lib.pa_cache_append(ctypes.byref(pool), 0, 256, 256, 256, 4, None) == _lib.PA_ENOTSUP
     del args
