@@ -376,6 +376,7 @@ def main():
                                "TFLOPs": round(fl / (ms_mix * 1e-3) / 1e12, 1)}
         del g5, s5
         torch.cuda.empty_cache()
+        rows["prefix_cache"] = prefix_cache_row(torch, pa, np)
         out["rows"] = rows
 
     # ---------------------------------------------------------- CPU oracle baseline
@@ -384,6 +385,61 @@ def main():
     out["wall_s"] = round(time.time() - t_start, 1)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def prefix_cache_row(torch, pa, np):
+    """The page's prefix-cache workload: a 3,000-token shared prefix plus 32
+    unique tokens per request, block 16, 32 query / 8 KV heads, head_dim 128.
+    Host: what admitting one request costs in the library's manager (add the
+    sequence through the prefix cache, append the uncached rest of the prompt
+    with its token ids), through the Python binding, for a request that hits
+    2,992 cached tokens and for one that hits none.  GPU: the prefill a hit
+    leaves (40 positions after 2,992 cached ones) against the whole prompt."""
+    bs, H_kv, H_q, d, N = 16, 8, 32, 128, 8192
+    rng = np.random.default_rng(7)
+    prefix = [int(x) for x in rng.integers(0, 150000, 3000)]
+    bm = pa.BlockManager(N, bs, rng.permutation(N))
+    first = prefix + [int(x) for x in rng.integers(0, 150000, 32)]
+    bm.add_seq_prefix(0, first)
+    bm.append_tokens(0, first)
+    reps, seq = 50, 1
+    prompts = [prefix + [int(x) for x in rng.integers(0, 150000, 32)] for _ in range(reps)]
+    misses = [[int(x) for x in rng.integers(0, 150000, 3032)] for _ in range(reps)]
+    t0 = time.perf_counter()
+    for pr in prompts:
+        hit = bm.add_seq_prefix(seq, pr)
+        bm.append_tokens(seq, pr[hit:])
+        seq += 1
+    t_hit = (time.perf_counter() - t0) / reps
+    for s_ in range(1, seq):
+        bm.free_seq(s_)
+    t0 = time.perf_counter()
+    for pr in misses:
+        bm.add_seq_prefix(seq, pr)
+        bm.append_tokens(seq, pr)
+        bm.free_seq(seq)
+        seq += 1
+    t_miss = (time.perf_counter() - t0) / reps
+    assert hit == 2992
+
+    pool = pa.KVPool(1, H_kv, 200, bs, d, "bf16", device="cuda")
+    pool.k.normal_()
+    pool.v.normal_()
+    table = torch.from_numpy(rng.permutation(200)[:190].astype(np.int32)).cuda()
+    scale = float(1 / np.sqrt(d))
+    qf = torch.randn(3032, H_q, d, device="cuda").to(torch.bfloat16)
+    of = torch.empty_like(qf)
+    qh, oh = qf[-40:].contiguous(), torch.empty_like(qf[-40:])
+    ms_full = time_loop(torch, lambda i: pa.pa_prefill_chunk(pool, 0, of, qf, table, 0, scale), 20, 3)
+    ws = pa.prefill_workspace(pool, 40, H_q, 2992)
+    ms_hit = time_loop(torch, lambda i: pa.pa_prefill_chunk(pool, 0, oh, qh, table, 2992, scale, ws), 20, 3)
+    ms_hit_one = time_loop(torch, lambda i: pa.pa_prefill_chunk(pool, 0, oh, qh, table, 2992, scale), 20, 3)
+    return {"workload": "3,000-token shared prefix + 32-token tail per request, block 16, GQA 32/8, d 128",
+            "hit_tokens": hit, "host_admit_hit_us": round(t_hit * 1e6, 1),
+            "host_admit_miss_us": round(t_miss * 1e6, 1),
+            "prefill_whole_prompt_ms": round(ms_full, 5), "prefill_after_hit_ms": round(ms_hit, 5),
+            "prefill_after_hit_unsplit_ms": round(ms_hit_one, 5),
+            "prefill_speedup": round(ms_full / ms_hit, 1)}
 
 
 def cpu_baseline(seconds, dbytes):

@@ -146,6 +146,13 @@ int pa_decode_append(const pa_kv_pool* pool, int32_t layer, void* out, const voi
                      float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Workspace bytes pa_prefill_chunk can use to split a chunk over its keys
+ * (0 when it would not split).  Depends on host-side sizes and the current
+ * device's CU count only.
+ */
+size_t pa_prefill_workspace_size(const pa_kv_pool* pool, int32_t T, int32_t H_q, int32_t ctx_before);
+
+/*
  * Causal prefill chunk over paged K/V: a long prompt is processed in chunks
  * ([ttlab] "새 문제: 긴 프리필이 디코드를 멈춘다"); chunk row t sits at position
  * ctx_before + t and attends to positions 0 .. ctx_before + t of its own
@@ -153,10 +160,17 @@ int pa_decode_append(const pa_kv_pool* pool, int32_t layer, void* out, const voi
  * already be appended.  bf16 and f16 pools only (matrix cores).
  *   out, q: device [T][H_q][head_dim], pool dtype.
  *   block_table: device int32 [nb], nb >= ceil((ctx_before + T) / block_size).
+ *   workspace: optional device buffer.  A short chunk after a long context
+ *        (the rest of a prompt after a prefix-cache hit) has too few position
+ *        tiles to fill the GPU; given pa_prefill_workspace_size(...) bytes,
+ *        the call splits the keys over more workgroups and merges the splits
+ *        (a second, small launch).  NULL: no split, same result up to
+ *        rounding.  A non-NULL workspace smaller than needed is PA_ESPACE.
+ *        Contents need no initialisation; 16-byte aligned.
  */
 int pa_prefill_chunk(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t T, int32_t H_q,
-                     const int32_t* block_table, int32_t nb, int32_t ctx_before, float scale,
-                     hipStream_t stream);
+                     const int32_t* block_table, int32_t nb, int32_t ctx_before, float scale, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 /*
  * A mixed batch in one launch: the decode step of B sequences and one causal
@@ -232,6 +246,47 @@ int pa_bm_seq_len(pa_bm* bm, int32_t seq);  /* >= 0, or PA_ENOENT */
 int pa_bm_refcount(pa_bm* bm, int32_t block); /* >= 0, or PA_EINVAL */
 int pa_bm_num_free(pa_bm* bm);
 int pa_bm_free_list(pa_bm* bm, int32_t* out, int32_t cap); /* returns the count; copies up to cap */
+
+/*
+ * Automatic prefix caching ([ttlab] "4. 프리픽스 캐시"; [icarus] "支持块级共享"):
+ * a later request whose prompt starts like an earlier one reuses the blocks
+ * that already hold that prefix's K/V instead of computing them again.
+ *   - Every full block of a sequence whose token ids the manager knows gets
+ *     a key: sha256 over the previous block's key (32 zero bytes for the
+ *     first block), the block's token ids as little-endian int32 and the
+ *     sequence's ``extra`` (LoRA adapter, multimodal inputs, cache salt --
+ *     hashed by the caller into 64 bits) as a little-endian uint64.  Through
+ *     the previous key, a key stands for the whole prefix up to its block.
+ *   - Only full blocks are cached.  A key already cached under another block
+ *     leaves the new block uncached.
+ *   - A freed block keeps its key and contents while it waits in the free
+ *     queue (free_seq queues a sequence's blocks tail first); taking a block
+ *     from the front of the queue evicts its key, so the least recently
+ *     freed goes first.
+ *   - Sequences made by pa_bm_add_seq and appended with pa_bm_append_tokens
+ *     are keyed too (extra = 0).  pa_bm_append_slots or
+ *     pa_bm_append_slots_batch (no token ids) stops a sequence's keying;
+ *     the manager then behaves exactly as without caching.
+ */
+/* New sequence for a prompt: its table starts with the cached blocks of the
+ * prompt's longest cached run of full blocks (taken out of the free queue
+ * if they wait there; refcounts +1).  *n_hit_out = tokens those blocks hold
+ * (a multiple of block_size).  The caller appends the rest of the prompt
+ * with pa_bm_append_tokens.  Takes no free block, so it cannot fail with
+ * PA_ENOMEM. */
+int pa_bm_add_seq_prefix(pa_bm* bm, int32_t seq, const int32_t* tokens, int32_t n, uint64_t extra,
+                         int32_t* n_hit_out);
+/* pa_bm_append_slots for the given token ids (host int32 [n]); every block
+ * the append fills is keyed and cached. */
+int pa_bm_append_tokens(pa_bm* bm, int32_t seq, const int32_t* tokens, int32_t n, int32_t* slots_out,
+                        int32_t* cow_pairs_out, int32_t* n_cow_out);
+/* Prompt tokens a new request would find cached (>= 0); no state change. */
+int pa_bm_prefix_lookup(pa_bm* bm, const int32_t* tokens, int32_t n, uint64_t extra);
+int pa_bm_num_cached(pa_bm* bm); /* blocks with a cached key */
+/* 1 and the 32-byte key in key_out if the block is cached, 0 if not. */
+int pa_bm_block_key(pa_bm* bm, int32_t block, uint8_t* key_out);
+/* SHA-256 (FIPS 180-4) of n bytes, the hash behind the block keys. */
+int pa_sha256(const void* data, size_t n, uint8_t* digest_out);
 
 #ifdef __cplusplus
 }

@@ -24,12 +24,43 @@ Readings where the pages leave a choice (each listed in the design notes):
   * Running out of blocks fails the whole request and leaves the allocator
     exactly as it was.
 
+Automatic prefix caching ([ttlab] "4. 프리픽스 캐시"; [icarus] "支持块级共享":
+full KV blocks are hashed so a later request with the same prefix reuses the
+computed K/V):
+  * every full block gets a key = hash(the previous block's key, this block's
+    token ids, extra information such as a cache salt); through the previous
+    key, one key stands for the whole prefix up to that block, so equal
+    tokens after different prefixes get different keys;
+  * only full blocks are cached;
+  * a finished request's blocks are not wiped: they wait in the free queue
+    with their contents and keys ("empty but still holding content"), queued
+    tail first, and the least recently used is evicted when a block is
+    needed;
+  * the hash is sha256.
+Readings where the pages leave a choice (listed in the design notes): the
+first block's previous key is 32 zero bytes; the hashed bytes are the
+previous key, the block's token ids as little-endian int32 and the extra
+information as one little-endian uint64; a block whose key is already cached
+under another block stays uncached; a cache hit takes the block out of the
+free queue wherever it sits; a sequence appended without token ids
+(append_slots) is no longer keyed.
+
 Processing is token by token, in the order the text describes, with a
 snapshot taken before each request for the all-or-nothing failure.
 """
 
 import copy
+import hashlib
+import struct
 from collections import deque
+
+ROOT_KEY = bytes(32)
+
+
+def block_key(prev_key, tokens, extra):
+    """Key of one full block: sha256(previous key, token ids, extra)."""
+    data = prev_key + struct.pack(f"<{len(tokens)}i", *[int(t) for t in tokens]) + struct.pack("<Q", int(extra))
+    return hashlib.sha256(data).digest()
 
 
 class OutOfBlocks(Exception):
@@ -49,13 +80,54 @@ class BlockManager:
         self.ref = [0] * self.num_blocks
         self.table = {}
         self.length = {}
+        # prefix cache: key -> block, block -> key, and per sequence the
+        # keying state: (extra, key of its last full block, token ids of its
+        # partly filled block), or None once it is no longer keyed
+        self.cache = {}
+        self.key_of = {}
+        self.keyed = {}
 
     # -- sequences ---------------------------------------------------------
-    def add_seq(self, seq):
+    def add_seq(self, seq, extra=0):
         if seq in self.table:
             raise KeyError(f"sequence {seq} exists")
         self.table[seq] = []
         self.length[seq] = 0
+        self.keyed[seq] = (int(extra), ROOT_KEY, [])
+
+    def add_seq_prefix(self, seq, tokens, extra=0):
+        """A new sequence for a prompt: its table starts with the cached
+        blocks of the prompt's longest cached prefix of full blocks.  Returns
+        the number of prompt tokens those blocks hold; the caller appends the
+        rest with append_tokens."""
+        self.add_seq(seq, extra)
+        bs = self.block_size
+        prev = ROOT_KEY
+        for j in range(len(tokens) // bs):
+            key = block_key(prev, tokens[j * bs:(j + 1) * bs], extra)
+            b = self.cache.get(key)
+            if b is None:
+                break
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+            self.table[seq].append(b)
+            self.length[seq] += bs
+            prev = key
+        self.keyed[seq] = (int(extra), prev, [])
+        return self.length[seq]
+
+    def prefix_lookup(self, tokens, extra=0):
+        """Prompt tokens a new request would find cached (no state change)."""
+        bs = self.block_size
+        prev, hit = ROOT_KEY, 0
+        for j in range(len(tokens) // bs):
+            key = block_key(prev, tokens[j * bs:(j + 1) * bs], extra)
+            if key not in self.cache:
+                break
+            hit += bs
+            prev = key
+        return hit
 
     def fork(self, parent, child):
         """child shares every block of parent (parallel sampling / beam search)."""
@@ -65,11 +137,14 @@ class BlockManager:
         self.length[child] = self.length[parent]
         for b in self.table[child]:
             self.ref[b] += 1
+        st = self.keyed[parent]
+        self.keyed[child] = None if st is None else (st[0], st[1], list(st[2]))
 
     def free_seq(self, seq):
         """Drop a finished sequence; blocks whose count reaches 0 rejoin the pool."""
         blocks = self.table.pop(seq)
         del self.length[seq]
+        del self.keyed[seq]
         for b in reversed(blocks):
             self.ref[b] -= 1
             if self.ref[b] == 0:
@@ -80,6 +155,8 @@ class BlockManager:
         if not self.free:
             raise OutOfBlocks()
         b = self.free.popleft()
+        if b in self.key_of:  # evict: its contents are about to be overwritten
+            del self.cache[self.key_of.pop(b)]
         self.ref[b] = 1
         return b
 
@@ -90,11 +167,26 @@ class BlockManager:
         for each new token in order, and the (source, destination) block pairs
         whose contents must be copied before the new tokens are written.
         Raises OutOfBlocks with no state change when the pool runs dry.
+        Without token ids the sequence's later blocks cannot be keyed.
         """
+        slots, pairs = self._append(seq, n, None)
+        self.keyed[seq] = None
+        return slots, pairs
+
+    def append_tokens(self, seq, tokens):
+        """append_slots for the given token ids; every block the append fills
+        is keyed and, unless its key is already cached, cached."""
+        return self._append(seq, len(tokens), [int(t) for t in tokens])
+
+    def _append(self, seq, n, tokens):
         if seq not in self.table:
             raise KeyError(f"no sequence {seq}")
-        snapshot = (copy.copy(self.free), list(self.ref), list(self.table[seq]), self.length[seq])
+        snapshot = (copy.copy(self.free), list(self.ref), list(self.table[seq]), self.length[seq],
+                    dict(self.cache), dict(self.key_of), self.keyed[seq])
         slots, pairs = [], []
+        st = self.keyed[seq]
+        if tokens is not None and st is not None:
+            st = (st[0], st[1], list(st[2]))
         try:
             tab = self.table[seq]
             for p in range(self.length[seq], self.length[seq] + n):
@@ -108,10 +200,22 @@ class BlockManager:
                     tab[j] = new
                     pairs.append((old, new))
                 slots.append(tab[j] * self.block_size + p % self.block_size)
+                if tokens is not None and st is not None:
+                    extra, prev, part = st
+                    part.append(tokens[p - self.length[seq]])
+                    if len(part) == self.block_size:  # block j is full: key it
+                        key = block_key(prev, part, extra)
+                        if key not in self.cache:
+                            self.cache[key] = tab[j]
+                            self.key_of[tab[j]] = key
+                        st = (extra, key, [])
         except OutOfBlocks:
-            self.free, self.ref, self.table[seq], self.length[seq] = snapshot
+            (self.free, self.ref, self.table[seq], self.length[seq], self.cache, self.key_of,
+             self.keyed[seq]) = snapshot
             raise
         self.length[seq] += n
+        if tokens is not None:
+            self.keyed[seq] = st
         return slots, pairs
 
     # -- inspection ----------------------------------------------------------
@@ -132,3 +236,10 @@ class BlockManager:
 
     def sequences(self):
         return sorted(self.table)
+
+    def num_cached(self):
+        return len(self.cache)
+
+    def block_key_of(self, b):
+        """The block's cache key, or None if it is not cached."""
+        return self.key_of.get(b)

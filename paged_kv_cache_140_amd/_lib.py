@@ -41,7 +41,9 @@ SIGNATURES = {
                                  ctypes.c_size_t, _p]),
     "pa_decode_append": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32,
                                         ctypes.c_float, _p, ctypes.c_size_t, _p]),
-    "pa_prefill_chunk": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _i32, ctypes.c_float, _p]),
+    "pa_prefill_workspace_size": (ctypes.c_size_t, [_PPOOL, _i32, _i32, _i32]),
+    "pa_prefill_chunk": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _i32, ctypes.c_float, _p,
+                                        ctypes.c_size_t, _p]),
     "pa_mixed_batch": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _p, _p, _i32, _p, _i32,
                                       _i32, ctypes.c_float, _i32, _p, ctypes.c_size_t, _p]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -58,6 +60,12 @@ SIGNATURES = {
     "pa_bm_refcount": (ctypes.c_int, [_p, _i32]),
     "pa_bm_num_free": (ctypes.c_int, [_p]),
     "pa_bm_free_list": (ctypes.c_int, [_p, _pi32, _i32]),
+    "pa_bm_add_seq_prefix": (ctypes.c_int, [_p, _i32, _pi32, _i32, ctypes.c_uint64, _pi32]),
+    "pa_bm_append_tokens": (ctypes.c_int, [_p, _i32, _pi32, _i32, _pi32, _pi32, _pi32]),
+    "pa_bm_prefix_lookup": (ctypes.c_int, [_p, _pi32, _i32, ctypes.c_uint64]),
+    "pa_bm_num_cached": (ctypes.c_int, [_p]),
+    "pa_bm_block_key": (ctypes.c_int, [_p, _i32, ctypes.c_char_p]),
+    "pa_sha256": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p]),
 }
 
 _lib = None

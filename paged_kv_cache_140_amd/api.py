@@ -134,17 +134,35 @@ def pa_decode_append(pool, layer, out, q, k_new, v_new, slot_mapping, block_tabl
                                  _stream(stream)), "pa_decode_append")
 
 
-def pa_prefill_chunk(pool, layer, out, q, block_table, ctx_before, scale, stream=None):
+def pa_prefill_workspace_size(pool, T, H_q, ctx_before):
+    s = pool.struct()
+    return int(lib().pa_prefill_workspace_size(ctypes.byref(s), int(T), int(H_q), int(ctx_before)))
+
+
+def prefill_workspace(pool, T, H_q, ctx_before, device="cuda"):
+    """A workspace tensor that lets pa_prefill_chunk split a short chunk over
+    its keys (None when it would not split)."""
+    n = pa_prefill_workspace_size(pool, T, H_q, ctx_before)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pa_prefill_chunk(pool, layer, out, q, block_table, ctx_before, scale, workspace=None, stream=None):
     T, H_q, d = (int(x) for x in q.shape)
     _need(q, "q", pool.torch_dtype, (T, H_q, pool.head_dim))
     _need(out, "out", pool.torch_dtype, (T, H_q, pool.head_dim))
     _need(block_table, "block_table", torch.int32)
     if block_table.dim() != 1:
         raise ValueError("block_table must be 1-D")
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
     s = pool.struct()
     check(lib().pa_prefill_chunk(ctypes.byref(s), layer, _ptr(out), _ptr(q), T, H_q, _ptr(block_table),
-                                 int(block_table.shape[0]), int(ctx_before), float(scale), _stream(stream)),
-          "pa_prefill_chunk")
+                                 int(block_table.shape[0]), int(ctx_before), float(scale), _ptr(workspace), ws_bytes,
+                                 _stream(stream)), "pa_prefill_chunk")
 
 
 def pa_mixed_batch(pool, layer, dec_out, dec_q, block_tables, context_lens, max_ctx, pf_out, pf_q, pf_table,
@@ -175,6 +193,14 @@ def pa_mixed_batch(pool, layer, dec_out, dec_q, block_tables, context_lens, max_
                                _ptr(pf_q), T, _ptr(pf_table), int(pf_table.shape[0]), int(ctx_before), float(scale),
                                int(prefill_workgroups), _ptr(workspace), ws_bytes, _stream(stream)),
           "pa_mixed_batch")
+
+
+def pa_sha256(data):
+    """SHA-256 digest (32 bytes) of ``data``, computed by the library."""
+    data = bytes(data)
+    out = ctypes.create_string_buffer(32)
+    check(lib().pa_sha256(data, len(data), out), "pa_sha256")
+    return out.raw
 
 
 def decode_workspace(pool, B, H_q, max_ctx, device="cuda"):
@@ -236,6 +262,46 @@ class BlockManager:
         self._check(lib().pa_bm_append_slots(self._h, int(seq), int(n), ps, pp, ctypes.byref(npair)),
                     "pa_bm_append_slots")
         return slots[:int(n)].copy(), ([(int(pair[0]), int(pair[1]))] if npair.value else [])
+
+    # -- prefix cache --------------------------------------------------------
+    def add_seq_prefix(self, seq, tokens, extra=0):
+        """New sequence for a prompt; returns the prompt tokens its cached
+        prefix blocks already hold."""
+        toks, tp = _arr(np.asarray(tokens) if len(tokens) else np.zeros(1))
+        hit = ctypes.c_int32(0)
+        self._check(lib().pa_bm_add_seq_prefix(self._h, int(seq), tp, len(tokens), int(extra) & (2**64 - 1),
+                                               ctypes.byref(hit)), "pa_bm_add_seq_prefix")
+        return hit.value
+
+    def append_tokens(self, seq, tokens):
+        """append_slots for these token ids (full blocks get cached) ->
+        (slots int32 [n], list of (src, dst) pairs)."""
+        n = len(tokens)
+        toks, tp = _arr(np.asarray(tokens) if n else np.zeros(1))
+        slots, ps = _arr(np.zeros(max(n, 1)))
+        pair, pp = _arr(np.zeros(2))
+        npair = ctypes.c_int32(0)
+        self._check(lib().pa_bm_append_tokens(self._h, int(seq), tp, n, ps, pp, ctypes.byref(npair)),
+                    "pa_bm_append_tokens")
+        return slots[:n].copy(), ([(int(pair[0]), int(pair[1]))] if npair.value else [])
+
+    def prefix_lookup(self, tokens, extra=0):
+        toks, tp = _arr(np.asarray(tokens) if len(tokens) else np.zeros(1))
+        st = lib().pa_bm_prefix_lookup(self._h, tp, len(tokens), int(extra) & (2**64 - 1))
+        if st < 0:
+            self._check(st, "pa_bm_prefix_lookup")
+        return st
+
+    def num_cached(self):
+        return lib().pa_bm_num_cached(self._h)
+
+    def block_key_of(self, block):
+        """The block's 32-byte cache key, or None if it is not cached."""
+        buf = ctypes.create_string_buffer(32)
+        st = lib().pa_bm_block_key(self._h, int(block), buf)
+        if st < 0:
+            self._check(st, "pa_bm_block_key")
+        return buf.raw if st == 1 else None
 
     def append_slots_batch(self, seqs, ns):
         """All-or-nothing batch -> (slots int32 [sum ns], pairs int32 [k][2])."""

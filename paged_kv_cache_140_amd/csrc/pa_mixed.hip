@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
       const int w = (k % H_kv) * ntiles + k / H_kv;
       if (r > 0) __syncthreads();  // the previous item's output staging is read
       prefill_tile<E, D, G, BS>(w, lds, pool_k, pool_v, layer_off, head_stride, pq, pout, ptable, T, H_q,
-                                ctx_before, scale_log2);
+                                ctx_before, scale_log2, 0, INT32_MAX, nullptr, nullptr);
     }
     return;
   }

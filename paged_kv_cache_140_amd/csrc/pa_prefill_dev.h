@@ -131,12 +131,20 @@ using PrefillLds = char[4][kKeysPerStep * D * 2];
 // holds positions [(ntiles - 1 - i) * TP, ...) (the tiles of a head run
 // last-first, since later positions see more keys).  The caller passes
 // the workgroup's LDS and, between two items, a workgroup barrier.
+//
+// Split over the keys: the item covers its 64-key steps [step_lo, step_hi)
+// only (clamped to the steps its rows can see; an empty range returns at
+// once) and, with ws_o set, writes its rows' un-normalised output (fp32,
+// [T][H_q][D] per split at ws_o) and (running max, sum) pairs ([T][H_q][2]
+// at ws_ml) instead of the output; a merge combines the splits.  Without a
+// split: step_lo = 0, step_hi >= every item's steps, ws_o = nullptr.
 template <typename E, int D, int G, int BS>
 __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const char* __restrict__ pool_k,
                                              const char* __restrict__ pool_v, int64_t layer_off, int64_t head_stride,
                                              const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                                              const int32_t* __restrict__ table, int32_t T, int32_t H_q,
-                                             int32_t ctx_before, float scale_log2) {
+                                             int32_t ctx_before, float scale_log2, int step_lo, int step_hi,
+                                             float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   using M = Mfma<E>;
   using vec = typename M::vec;
   constexpr int ROWS = kRowsPerWave * kPrefillWaves;  // query rows per workgroup
@@ -166,7 +174,10 @@ __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const ch
   const int h = lane >> 5;
   const int t_last = min(t0 + TP, T) - 1;
   const int kmax = ctx_before + t_last + 1;  // no row of this workgroup sees key kmax or later
-  const int nsteps = (kmax + KT - 1) / KT;
+  // local steps 0 .. nsteps-1 are the item's 64-key steps s0 .. s0+nsteps-1
+  const int s0 = step_lo;
+  const int nsteps = min((kmax + KT - 1) / KT, step_hi) - s0;
+  if (nsteps <= 0) return;  // uniform: this split holds none of the item's keys
   const int first_masked_key = ctx_before + t0 + 1;
   // Waves 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise and run
   // the same work one phase apart.
@@ -203,12 +214,12 @@ __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const ch
   // clamping the key first keeps every clamped row's block.
   auto fetch = [&](int step) __attribute__((always_inline)) {
     Blocks b;
-    b.lo = table[min(step * KT + rg * 16, kmax - 1) / BS];
-    b.hi = BS >= 16 ? b.lo : table[min(step * KT + rg * 16 + 8, kmax - 1) / BS];
+    b.lo = table[min((s0 + step) * KT + rg * 16, kmax - 1) / BS];
+    b.hi = BS >= 16 ? b.lo : table[min((s0 + step) * KT + rg * 16 + 8, kmax - 1) / BS];
     return b;
   };
   auto issue = [&](const char* base, int step, const Blocks& bl, char* dst) __attribute__((always_inline)) {
-    const int key = min(step * KT + lrow, kmax - 1);
+    const int key = min((s0 + step) * KT + lrow, kmax - 1);
     const int64_t blk = (BS >= 16 || (lane >> 2) < 8) ? bl.lo : bl.hi;
     const char* src = base + (blk * BS + (key & (BS - 1))) * ROWB + lchunk;
 #pragma unroll
@@ -307,7 +318,7 @@ __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const ch
   // n*32 + 16s + 4h + [0,4) and n*32 + 16s + 8 + 4h + [0,4): score values
   // 8s .. 8s+7 of tile n.
   auto softmax = [&](int j) __attribute__((always_inline)) {
-    const int key0 = j * KT;
+    const int key0 = (s0 + j) * KT;
     if (scale_log2 <= 0.0f) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) st[n] *= scale_log2;
@@ -412,11 +423,27 @@ __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const ch
   }
   if (!group_b) barrier_keep_loads();
 
+  const float lt = sum_halves(lsum);
+  if (ws_o) {
+    // A split: the row's un-normalised output, running max and sum (rows
+    // that see none of this split's keys leave m = -inf, l = 0, o = 0).
+    if (pos < T) {
+      const int64_t row = static_cast<int64_t>(pos) * H_q + g * G + r % G;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(ws_o + row * D + dt * 32 + 8 * j + 4 * h) =
+              make_float4(o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]);
+      if (h == 0) *reinterpret_cast<float2*>(ws_ml + 2 * row) = make_float2(m, lt);
+    }
+    return;
+  }
+
   // Normalise; stage the wave's 32 x D output rows in LDS (two waves per
   // tile array, no longer read) and write whole rows.  The lane holds dims
   // dt*32 + 8*j + 4*h + [0,4) of row li, j = 0..3; chunk c of row rr is
   // stored at chunk position c ^ (rr % DCH).
-  const float lt = sum_halves(lsum);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   char* ob = &lds[wave >> 1][(wave & 1) * kRowsPerWave * ROWB];
 #pragma unroll

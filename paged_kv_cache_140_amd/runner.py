@@ -14,7 +14,7 @@ import torch
 from pa_inputs import gen
 
 from .api import (BlockManager, KVPool, OutOfBlocks, TORCH_DTYPE, decode_workspace, pa_cache_append,
-                  pa_copy_blocks, pa_decode, pa_decode_append, pa_mixed_batch, pa_prefill_chunk)
+                  pa_copy_blocks, pa_decode, pa_decode_append, pa_mixed_batch, pa_prefill_chunk, prefill_workspace)
 
 
 def to_device(x, dtype, device):
@@ -35,7 +35,7 @@ class StepInputs:
     max_ctx: int
     out: torch.Tensor
     workspace: object
-    prefill: object = None  # (q, table, ctx_before, out)
+    prefill: object = None  # (q, table, ctx_before, out, workspace)
     n_pairs: int = 0
     # True when the step appends exactly one token to each decoded sequence,
     # in decode order: then append + decode can run as one pa_decode_append.
@@ -128,7 +128,8 @@ class GpuRun:
             pf = step.prefill
             table = np.array(self.bm.block_table(pf.seq), dtype=np.int32)
             q = to_device(pf.q, cfg["dtype"], dev)
-            si.prefill = (q, torch.from_numpy(table).to(dev), pf.ctx_before, torch.empty_like(q))
+            ws = prefill_workspace(self.pool, pf.T, cfg["H_q"], pf.ctx_before, dev)
+            si.prefill = (q, torch.from_numpy(table).to(dev), pf.ctx_before, torch.empty_like(q), ws)
         return si
 
     def launch(self, si, stream=None, do_copy=True, do_append=True, do_decode=True, do_prefill=True, fused=False,
@@ -144,7 +145,7 @@ class GpuRun:
                 pa_copy_blocks(self.pool, si.pairs, stream)
             if do_append and si.slots.numel():
                 pa_cache_append(self.pool, self.layer, si.k_new, si.v_new, si.slots, stream)
-            q, table, ctx_before, out = si.prefill
+            q, table, ctx_before, out, _ = si.prefill
             pa_mixed_batch(self.pool, self.layer, si.out, si.q, si.tables, si.lens, si.max_ctx, out, q, table,
                            ctx_before, cfg["scale"], prefill_workgroups, si.workspace, stream)
             return
@@ -160,8 +161,8 @@ class GpuRun:
             pa_decode(self.pool, self.layer, si.out, si.q, si.tables, si.lens, si.max_ctx, cfg["scale"],
                       si.workspace, stream)
         if do_prefill and si.prefill is not None:
-            q, table, ctx_before, out = si.prefill
-            pa_prefill_chunk(self.pool, self.layer, out, q, table, ctx_before, cfg["scale"], stream)
+            q, table, ctx_before, out, ws = si.prefill
+            pa_prefill_chunk(self.pool, self.layer, out, q, table, ctx_before, cfg["scale"], ws, stream)
 
     def run_step(self, step, fused=False):
         si = self.prepare(step)

@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_hot_path():
     names = declared_functions()
     for n in ("pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_append", "pa_prefill_chunk",
-              "pa_mixed_batch", "pa_decode_workspace_size",
+              "pa_mixed_batch", "pa_decode_workspace_size", "pa_prefill_workspace_size",
               "pa_status_string", "pa_bm_create", "pa_bm_append_slots", "pa_bm_fork", "pa_bm_free_seq"):
         assert n in names
 
@@ -101,3 +101,7 @@ def test_workspace_size_is_zero_or_enough():
     big = lib.pa_decode_workspace_size(ctypes.byref(pool), 63, 64, 32769)
     assert big >= 63 * 64 * 2 * (128 + 2) * 4
     assert lib.pa_decode_workspace_size(ctypes.byref(pool), 0, 64, 100) == 0
+    # a prefill chunk splits over its keys only when its position tiles are few
+    assert lib.pa_prefill_workspace_size(ctypes.byref(pool), 40, 32, 2992) >= 2 * 40 * 32 * (128 + 2) * 4
+    assert lib.pa_prefill_workspace_size(ctypes.byref(pool), 1024, 64, 3500) == 0
+    assert lib.pa_prefill_workspace_size(ctypes.byref(pool), 0, 64, 3500) == 0

@@ -31,14 +31,19 @@ def _chunk_world(rng, total, H_kv, d, bs, dtype, extra_blocks=9):
     return op, gp, bm.block_table(0)
 
 
-def _run(gp, q32, table, ctx_before, scale, dtype, pad_table=0):
-    from paged_kv_cache_140_amd import pa_prefill_chunk
+def _run(gp, q32, table, ctx_before, scale, dtype, pad_table=0, split=False):
+    """split: pass the workspace, so that a chunk with few position tiles is
+    cut over its keys and merged."""
+    from paged_kv_cache_140_amd import pa_prefill_chunk, prefill_workspace
     from paged_kv_cache_140_amd.runner import to_device
 
     q = to_device(q32, dtype, "cuda")
     out = torch.full_like(q, float("nan"))
     tab = np.asarray(list(table) + [0] * pad_table, dtype=np.int32)
-    pa_prefill_chunk(gp, 0, out, q, torch.from_numpy(tab).cuda(), ctx_before, scale)
+    ws = prefill_workspace(gp, q.shape[0], q.shape[1], ctx_before) if split else None
+    if ws is not None:
+        ws.fill_(255)  # NaN patterns: a merge that read an unwritten split would show
+    pa_prefill_chunk(gp, 0, out, q, torch.from_numpy(tab).cuda(), ctx_before, scale, ws)
     torch.cuda.synchronize()
     return out
 
@@ -58,14 +63,15 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[4]}-hq{c[0]}-hkv{c[1]}-d{c[2]}-bs{c[3]}-c{c[5]}-t{c[6]}"
                                              for c in CASES])
-def test_prefill_chunk_small(case):
+@pytest.mark.parametrize("split", [False, True], ids=["one-pass", "key-split"])
+def test_prefill_chunk_small(case, split):
     H_q, H_kv, d, bs, dtype, ctx_before, T = case
     rng = np.random.default_rng(ctx_before * 31 + T)
-    say("prefill", case)
+    say("prefill", case, "split" if split else "")
     op, gp, table = _chunk_world(rng, ctx_before + T, H_kv, d, bs, dtype)
     q32 = rng.standard_normal((T, H_q, d)).astype(np.float32)
     scale = float(np.float32(1 / np.sqrt(d)))
-    out = _run(gp, q32, table, ctx_before, scale, dtype, pad_table=3)
+    out = _run(gp, q32, table, ctx_before, scale, dtype, pad_table=3, split=split)
     ref = attention.prefill_chunk(op, 0, widen(q32, dtype), table, ctx_before, scale)
     err = max_abs_err(f64(out), ref)
     say("  max abs err", err)
@@ -112,5 +118,26 @@ def test_prefill_chunk_of_the_mixed_workload():
     rows = [0, 3, 511, 1023]
     ref = attention.causal_rows(widen(pf.q, "bf16"), kc, vc, pf.ctx_before, scn.cfg["scale"], rows)
     err = max_abs_err(got, ref, rows)
+    say("  max abs err", err)
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("H_q,T,ctx_before", [(32, 40, 2992), (64, 1, 4000), (8, 200, 6000), (16, 129, 1000)])
+def test_prefill_short_chunk_after_long_context_split(H_q, T, ctx_before):
+    """The rest of a prompt after a prefix-cache hit (40 rows after 2,992
+    cached tokens) and other short chunks over long contexts: run split over
+    the keys, every row against the oracle."""
+    from paged_kv_cache_140_amd import pa_prefill_workspace_size
+
+    rng = np.random.default_rng(T + ctx_before)
+    H_kv, d, bs = 8, 128, 16
+    say("prefill split", H_q, T, ctx_before)
+    op, gp, table = _chunk_world(rng, ctx_before + T, H_kv, d, bs, "bf16")
+    assert pa_prefill_workspace_size(gp, T, H_q, ctx_before) > 0
+    q32 = rng.standard_normal((T, H_q, d)).astype(np.float32)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    out = f64(_run(gp, q32, table, ctx_before, scale, "bf16", split=True))
+    ref = attention.prefill_chunk(op, 0, widen(q32, "bf16"), table, ctx_before, scale)
+    err = max_abs_err(out, ref)
     say("  max abs err", err)
     assert err <= TOL["bf16"]
