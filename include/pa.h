@@ -248,6 +248,23 @@ int pa_bm_num_free(pa_bm* bm);
 int pa_bm_free_list(pa_bm* bm, int32_t* out, int32_t cap); /* returns the count; copies up to cap */
 
 /*
+ * Capacity queries for admission and preemption: the block is the unit of
+ * capacity, so a scheduler admits, waits or preempts by comparing these
+ * with pa_bm_num_free ([icarus] "改善调度与回收"; [ttlab] "5. KV 자리가
+ * 모자라면": a request that does not fit waits, and when even running
+ * requests run short one of them gives its KV back and is computed again
+ * later).  No state change.
+ */
+/* Free blocks pa_bm_append_slots(seq, n) would take: one per new logical
+ * block, plus one when the partly filled last block is shared (>= 0). */
+int pa_bm_blocks_needed(pa_bm* bm, int32_t seq, int32_t n);
+/* Free-queue blocks that admitting this prompt would take
+ * (pa_bm_add_seq_prefix, then pa_bm_append_tokens of the rest): cached
+ * blocks of its prefix that wait in the free queue, plus a block for each
+ * of the rest (>= 0). */
+int pa_bm_admit_cost(pa_bm* bm, const int32_t* tokens, int32_t n, uint64_t extra);
+
+/*
  * Automatic prefix caching ([ttlab] "4. 프리픽스 캐시"; [icarus] "支持块级共享"):
  * a later request whose prompt starts like an earlier one reuses the blocks
  * that already hold that prefix's K/V instead of computing them again.

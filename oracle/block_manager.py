@@ -117,6 +117,33 @@ class BlockManager:
         self.keyed[seq] = (int(extra), prev, [])
         return self.length[seq]
 
+    def blocks_needed(self, seq, n):
+        """Free blocks append_slots(seq, n) would take: the new logical blocks
+        it reaches, and one more when its partly filled last block is
+        shared (copy-on-write)."""
+        bs, tab, ln = self.block_size, self.table[seq], self.length[seq]
+        if n <= 0:
+            return 0
+        fresh = -(-(ln + n) // bs) - len(tab)
+        cow = 1 if ln % bs and self.ref[tab[-1]] > 1 else 0
+        return fresh + cow
+
+    def admit_cost(self, tokens, extra=0):
+        """Free-queue blocks that admitting a prompt takes: its cached prefix
+        blocks that wait in the free queue, and a fresh block for each block
+        of the rest."""
+        bs = self.block_size
+        prev, hits, waiting = ROOT_KEY, 0, 0
+        for j in range(len(tokens) // bs):
+            key = block_key(prev, tokens[j * bs:(j + 1) * bs], extra)
+            b = self.cache.get(key)
+            if b is None:
+                break
+            hits += 1
+            waiting += self.ref[b] == 0
+            prev = key
+        return waiting + -(-len(tokens) // bs) - hits
+
     def prefix_lookup(self, tokens, extra=0):
         """Prompt tokens a new request would find cached (no state change)."""
         bs = self.block_size

@@ -111,8 +111,22 @@ class OracleRun:
             else:
                 raise ValueError(op)
 
+    def run_ops(self, step):
+        """The step's forks and frees, before its appends."""
+        for op in step.ops:
+            if op[0] == "fork":
+                self.bm.fork(op[1], op[2])
+                self.logical[op[2]] = list(self.logical[op[1]])
+            elif op[0] == "free":
+                self.bm.free_seq(op[1])
+                del self.logical[op[1]]
+            else:
+                raise ValueError(op)
+
     def bookkeeping(self, step):
-        """Slots and copy-on-write pairs of a step's appends, in append order."""
+        """Slots and copy-on-write pairs of a step's appends, in append order
+        (after the step's forks and frees)."""
+        self.run_ops(step)
         slots, pairs = [], []
         for seq, n in step.appends:
             s, p = self.bm.append_slots(seq, n)

@@ -1,4 +1,4 @@
-"""Shape tables of the five synthetic workloads.
+"""Shape tables of the five synthetic workloads (and a beam-search one).
 
 Sizes only.  Which sequences exist, how long they are and what values their
 K/V hold are drawn in ``gen`` and laid out as an op list in ``scenario``.
@@ -76,6 +76,22 @@ CONFIGS = {
         chunk=1024,
         num_blocks=131072,
         kind="mixed",
+    ),
+    # Not one of the five headline workloads: beam search, where surviving
+    # beams fork from forks and shared blocks are copied on write at any depth.
+    6: dict(
+        name="beam-search",
+        dtype="bf16",
+        prompts=4,
+        beam=4,
+        prompt_len=200,  # 12 full blocks + 8 tokens: every first step copies on write
+        steps=24,
+        H_q=16,
+        H_kv=8,
+        d=128,
+        bs=16,
+        num_blocks=1024,
+        kind="beam",
     ),
 }
 

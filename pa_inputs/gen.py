@@ -6,12 +6,12 @@ regenerated alone (the full-size parity tests sample a few sequences).
 Purpose ids:
   0 lengths   1 free-block order   2 churn   3 history K/V (per sequence)
   4 new-token K/V (per step)   5 queries (per step)   6 prefill-chunk K/V
-  7 prefill-chunk queries
+  7 prefill-chunk queries   8 beam survivors (per step and prompt)
 """
 
 import numpy as np
 
-LENGTHS, FREE_ORDER, CHURN, HISTORY, NEW_KV, QUERY, CHUNK_KV, CHUNK_Q = range(8)
+LENGTHS, FREE_ORDER, CHURN, HISTORY, NEW_KV, QUERY, CHUNK_KV, CHUNK_Q, BEAM = range(9)
 
 
 def rng(seed, cid, purpose, *index):
@@ -75,6 +75,14 @@ def chunk_kv(cfg, seed, T):
 
 def chunk_queries(cfg, seed, T):
     return normal(rng(seed, cfg["id"], CHUNK_Q), (int(T), cfg["H_q"], cfg["d"]))
+
+
+def beam_parents(cfg, seed, step, group):
+    """Which current beam each of the next step's beams continues: ``beam``
+    indices drawn with replacement (a beam drawn twice forks, one not drawn
+    ends)."""
+    k = cfg["beam"]
+    return rng(seed, cfg["id"], BEAM, step, group).integers(0, k, size=k)
 
 
 def churn(cfg, seed, add, try_append, free):

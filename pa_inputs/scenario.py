@@ -12,7 +12,8 @@ Ops in ``setup``:
   ("fork", parent, child)             child shares all of parent's blocks
   ("churn",)                          run ``gen.churn`` against the allocator
 
-Each ``Step`` then: one batched append (``appends`` in order, K/V rows
+Each ``Step`` then: its ``ops`` (("fork", parent, child) and ("free", seq),
+in order), one batched append (``appends`` in order, K/V rows
 ``k_new``/``v_new`` in the same order, copy-on-write pairs first), then decode
 attention for ``decode_seqs`` with queries ``q`` and, when present, one causal
 prefill chunk.
@@ -43,6 +44,7 @@ class Step:
     decode_seqs: List[int]
     q: np.ndarray  # float32 [len(decode_seqs)][H_q][d]
     prefill: Optional[Prefill] = None
+    ops: list = field(default_factory=list)  # forks and frees before the appends
 
 
 @dataclass
@@ -113,6 +115,41 @@ def build_scenario(cid, seed=0, **overrides):
         st.prefill = Prefill(seq=pseq, ctx_before=cfg["ctx_before"], T=cfg["chunk"],
                              q=gen.chunk_queries(cfg, seed, cfg["chunk"]))
         scn.steps.append(st)
+    elif kind == "beam":
+        # Every prompt starts ``beam`` beams sharing its blocks (its last one
+        # partly filled).  Each step the next beams are drawn from the current
+        # ones with replacement: a beam drawn first keeps its sequence, each
+        # further draw forks it, and a beam not drawn is freed; then every
+        # beam appends one token and is decoded.
+        P, k = cfg["prompts"], cfg["beam"]
+        beams, next_id = [], []
+        for p in range(P):
+            root = p * 1000
+            scn.setup.append(("add", root))
+            scn.setup.append(("append", root, cfg["prompt_len"]))
+            for j in range(1, k):
+                scn.setup.append(("fork", root, root + j))
+            beams.append([root + j for j in range(k)])
+            next_id.append(root + k)
+        for t in range(cfg["steps"]):
+            ops = []
+            for p in range(P):
+                kept, new = set(), []
+                for i in gen.beam_parents(cfg, seed, t, p):
+                    parent = beams[p][int(i)]
+                    if parent not in kept:
+                        kept.add(parent)
+                        new.append(parent)
+                    else:
+                        ops.append(("fork", parent, next_id[p]))
+                        new.append(next_id[p])
+                        next_id[p] += 1
+                ops += [("free", b) for b in beams[p] if b not in kept]
+                beams[p] = sorted(new)
+            st = _decode_batch(cfg, seed, sorted(b for bs_ in beams for b in bs_), t)
+            st.ops = ops
+            scn.steps.append(st)
+        scn.ctx = np.full(P * k, cfg["prompt_len"], dtype=np.int64)
     else:
         raise ValueError(kind)
     return scn

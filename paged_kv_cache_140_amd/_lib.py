@@ -64,6 +64,8 @@ SIGNATURES = {
     "pa_bm_append_tokens": (ctypes.c_int, [_p, _i32, _pi32, _i32, _pi32, _pi32, _pi32]),
     "pa_bm_prefix_lookup": (ctypes.c_int, [_p, _pi32, _i32, ctypes.c_uint64]),
     "pa_bm_num_cached": (ctypes.c_int, [_p]),
+    "pa_bm_blocks_needed": (ctypes.c_int, [_p, _i32, _i32]),
+    "pa_bm_admit_cost": (ctypes.c_int, [_p, _pi32, _i32, ctypes.c_uint64]),
     "pa_bm_block_key": (ctypes.c_int, [_p, _i32, ctypes.c_char_p]),
     "pa_sha256": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p]),
 }

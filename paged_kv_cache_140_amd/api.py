@@ -295,6 +295,21 @@ class BlockManager:
     def num_cached(self):
         return lib().pa_bm_num_cached(self._h)
 
+    def blocks_needed(self, seq, n):
+        """Free blocks append_slots(seq, n) would take."""
+        st = lib().pa_bm_blocks_needed(self._h, int(seq), int(n))
+        if st < 0:
+            self._check(st, "pa_bm_blocks_needed")
+        return st
+
+    def admit_cost(self, tokens, extra=0):
+        """Free-queue blocks admitting this prompt would take."""
+        toks, tp = _arr(np.asarray(tokens) if len(tokens) else np.zeros(1))
+        st = lib().pa_bm_admit_cost(self._h, tp, len(tokens), int(extra) & (2**64 - 1))
+        if st < 0:
+            self._check(st, "pa_bm_admit_cost")
+        return st
+
     def block_key_of(self, block):
         """The block's 32-byte cache key, or None if it is not cached."""
         buf = ctypes.create_string_buffer(32)

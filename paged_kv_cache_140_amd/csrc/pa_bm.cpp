@@ -577,6 +577,29 @@ int pa_bm_prefix_lookup(pa_bm* bm, const int32_t* tokens, int32_t n, uint64_t ex
   return hit;
 }
 
+int pa_bm_blocks_needed(pa_bm* bm, int32_t seq, int32_t n) {
+  if (!bm || n < 0) return pa::fail(PA_EINVAL, "NULL manager or negative token count");
+  Seq* s = bm->find(seq);
+  if (!s) return pa::fail(PA_ENOENT, "no sequence " + std::to_string(seq));
+  return static_cast<int>(bm->need(*s, n));
+}
+
+int pa_bm_admit_cost(pa_bm* bm, const int32_t* tokens, int32_t n, uint64_t extra) {
+  if (!bm || n < 0 || (n > 0 && !tokens)) return pa::fail(PA_EINVAL, "NULL argument or negative length");
+  const int32_t bs = bm->block_size;
+  Key prev{};
+  int64_t hits = 0, waiting = 0;
+  for (int32_t j = 0; j < n / bs; ++j) {
+    const Key k = block_key(prev, tokens + static_cast<int64_t>(j) * bs, bs, extra);
+    auto it = bm->cache.find(k);
+    if (it == bm->cache.end()) break;
+    ++hits;
+    if (bm->ref[it->second] == 0) ++waiting;
+    prev = k;
+  }
+  return static_cast<int>(waiting + pa::ceil_div(n, bs) - hits);
+}
+
 int pa_bm_num_cached(pa_bm* bm) {
   if (!bm) return pa::fail(PA_EINVAL, "NULL manager");
   return static_cast<int>(bm->cache.size());

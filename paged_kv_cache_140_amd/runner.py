@@ -100,8 +100,16 @@ class GpuRun:
 
     # -- one step ------------------------------------------------------------
     def prepare(self, step):
-        """Host bookkeeping for ``step`` and H2D staging of all its inputs."""
+        """Host bookkeeping for ``step`` (its forks and frees, then its
+        appends) and H2D staging of all its inputs."""
         cfg, dev = self.cfg, self.device
+        for op in step.ops:
+            if op[0] == "fork":
+                self.bm.fork(op[1], op[2])
+            elif op[0] == "free":
+                self.bm.free_seq(op[1])
+            else:
+                raise ValueError(op)
         seqs = [s for s, _ in step.appends]
         ns = [n for _, n in step.appends]
         slots, pairs = self.bm.append_slots_batch(seqs, ns)

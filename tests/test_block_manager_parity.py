@@ -117,6 +117,11 @@ def _drive(scn, bm_factory, oob):
         elif op[0] == "churn":
             gen.churn(cfg, scn.seed, bm.add_seq, try_append, bm.free_seq)
     for st in scn.steps:
+        for op in st.ops:
+            if op[0] == "fork":
+                bm.fork(op[1], op[2])
+            else:
+                bm.free_seq(op[1])
         slots, pairs = [], []
         for s, n in st.appends:
             a, b = bm.append_slots(s, n)
@@ -127,7 +132,7 @@ def _drive(scn, bm_factory, oob):
 
 
 @pytest.mark.parametrize("cid,over", [(1, {}), (2, {}), (3, {"bs": 8}), (3, {"bs": 16}), (3, {"bs": 32}),
-                                      (4, {}), (5, {})])
+                                      (4, {}), (5, {}), (6, {})])
 def test_workload_bookkeeping_bit_exact(cid, over):
     scn = build_scenario(cid, 0, **over)
     bo, ro = _drive(scn, OracleBM, OracleOOB)

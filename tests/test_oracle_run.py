@@ -101,3 +101,27 @@ def test_config5_bookkeeping_and_chunk_rows():
     assert len(slots) == 63 + 1024 and pairs == []
     assert r.bm.seq_len(63) == 3500 + 1024
     assert len(r.bm.block_table(63)) == -(-4524 // 16)
+
+
+def test_beam_search_paged_equals_logical_every_step():
+    """Beam search: beams fork from forks and copy the shared partly filled
+    block on write at every depth; at each step every beam's paged decode
+    equals attention over its own logical K/V rows, bit for bit."""
+    from oracle import attention
+    from oracle.run import widen
+
+    scn = build_scenario(6, 0, prompts=2, prompt_len=40, steps=12, d=64)
+    r = OracleRun(scn)
+    r.run_setup()
+    forks = pairs = 0
+    for st in scn.steps:
+        forks += sum(op[0] == "fork" for op in st.ops)
+        res = r.run_step(st)
+        pairs += len(res.pairs)
+        q = widen(st.q, "bf16")
+        for i, seq in enumerate(st.decode_seqs):
+            np.testing.assert_array_equal(res.decode_out[i], attention.attend(q[i], *r.logical_kv(seq),
+                                                                              scn.cfg["scale"]))
+        # each prompt keeps exactly ``beam`` live beams
+        assert len(st.decode_seqs) == 2 * 4
+    assert forks > 0 and pairs > 0

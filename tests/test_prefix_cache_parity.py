@@ -56,6 +56,9 @@ def test_prefix_cache_ops_bit_exact(seed):
                 [int(t) for t in rng.integers(-3, 4, int(rng.integers(0, 3 * bs)))]
             extra = int(rng.choice([0, 1, 2**63 + 5]))
             assert o.prefix_lookup(prompt, extra) == l.prefix_lookup(prompt, extra)
+            cost = o.admit_cost(prompt, extra)
+            assert cost == l.admit_cost(prompt, extra)
+            free_before = o.num_free()
             ho, hl = o.add_seq_prefix(nxt, prompt, extra), l.add_seq_prefix(nxt, prompt, extra)
             assert ho == hl
             live.append(nxt)
@@ -64,7 +67,9 @@ def test_prefix_cache_ops_bit_exact(seed):
                 ok = True
             except OracleOOB:
                 ok = False
+            assert ok == (cost <= free_before)
             if ok:
+                assert free_before - o.num_free() == cost
                 sl, pl = l.append_tokens(nxt, prompt[ho:])
                 assert list(sl) == so and pl == po
             else:
@@ -84,12 +89,17 @@ def test_prefix_cache_ops_bit_exact(seed):
         elif x < 0.85:
             s = live[int(rng.integers(len(live)))]
             toks = [int(t) for t in rng.integers(-3, 4, int(rng.integers(0, 2 * bs + 2)))]
+            need = o.blocks_needed(s, len(toks))
+            assert need == l.blocks_needed(s, len(toks))
+            free_before = o.num_free()
             try:
                 so, po = o.append_tokens(s, toks)
                 ok = True
             except OracleOOB:
                 ok = False
+            assert ok == (need <= free_before)
             if ok:
+                assert free_before - o.num_free() == need
                 sl, pl = l.append_tokens(s, toks)
                 assert list(sl) == so and pl == po
             else:
