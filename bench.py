@@ -377,6 +377,7 @@ def main():
         del g5, s5
         torch.cuda.empty_cache()
         rows["prefix_cache"] = prefix_cache_row(torch, pa, np)
+        rows["capacity"] = capacity_row(pa, np)
         out["rows"] = rows
 
     # ---------------------------------------------------------- CPU oracle baseline
@@ -385,6 +386,30 @@ def main():
     out["wall_s"] = round(time.time() - t_start, 1)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def capacity_row(pa, np):
+    """KV slots that hold tokens: the library's block manager on the
+    13B-shaped workload's 64 lognormal lengths, against reserving 2,048
+    tokens per request as systems before paging did; and how many 512 + 128
+    token requests a 22,048-token KV pool holds either way (host only)."""
+    from pa_inputs import build_scenario
+
+    out = {"workload": "64 lognormal context lengths (median 400, clipped to [16, 2048]); 2,048-token reservation"}
+    for bs in (8, 16, 32):
+        scn = build_scenario(3, 0, bs=bs)
+        lens = [int(x) for x in scn.ctx]
+        bm = pa.BlockManager(sum(-(-n // bs) for n in lens), bs, np.arange(sum(-(-n // bs) for n in lens)))
+        for i, n in enumerate(lens):
+            bm.add_seq(i)
+            bm.append_slots(i, n)
+        slots = sum(len(bm.block_table(i)) for i in range(len(lens))) * bs
+        out[f"paged_bs{bs}_token_fraction"] = round(sum(lens) / slots, 4)
+        out[f"paged_bs{bs}_mean_waste_tokens"] = round((slots - sum(lens)) / len(lens), 2)
+    out["reserved_token_fraction"] = round(sum(lens) / (2048 * len(lens)), 4)
+    out["requests_in_22048_tokens_paged"] = 22048 // (-(-640 // 16) * 16)
+    out["requests_in_22048_tokens_reserved"] = 22048 // 2048
+    return out
 
 
 def prefix_cache_row(torch, pa, np):
