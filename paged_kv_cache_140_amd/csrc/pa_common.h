@@ -82,6 +82,10 @@ __device__ __forceinline__ void store_elem(F16, void* base, int64_t i, float v) 
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *static_cast<const uint4*>(p); }
 
+// Two 16-bit floats in one dword, for the packed dot products.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------- lanes
 // Cross-lane moves inside a row of 16 lanes through DPP (no LDS traffic).
 template <int CTRL>

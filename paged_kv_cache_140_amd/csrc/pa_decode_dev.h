@@ -63,8 +63,6 @@ __device__ __forceinline__ void pair_with(float x, float& a, float& b) {
   }
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // q.k over one lane's 16-byte chunk.  The query is kept in its storage
 // format; bf16 and f16 pairs go through the packed dot instructions (exact

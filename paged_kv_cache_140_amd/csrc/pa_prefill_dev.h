@@ -47,6 +47,9 @@ constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kKeysPerStep = 64;
+// How far (log2 units) a row's max may pass the softmax reference before the
+// prefill rescales its running sum and output: probabilities stay <= 256.
+constexpr float kSlack = 8.0f;
 
 // LDS tile layout for K and V (KT keys x D dims, 16-bit): columns of 64
 // bytes (4 chunks of 16 bytes, 32 dims) are stored one after another, each
@@ -337,8 +340,14 @@ __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const ch
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[n][v]);
     mx = max_halves(mx);
-    const float mnew = fmaxf(m, mx * c);
-    if (__any(mnew > m)) {
+    // The running max m is the exponent's reference: it is raised (and l,
+    // O rescaled) only when a row's max passes it by more than kSlack, so
+    // every probability stays <= 2^kSlack and, after the first few steps,
+    // the rescale is almost never taken.  l and O share the reference, so
+    // O / l is unchanged.
+    const float mcand = mx * c;
+    if (__any(mcand > m + kSlack)) {
+      const float mnew = fmaxf(m, mcand);
       const float alpha = __builtin_amdgcn_exp2f(m - ((mnew == -INFINITY) ? 0.0f : mnew));
       m = mnew;
       lsum *= alpha;
