@@ -18,8 +18,10 @@
  *   - Return value: PA_OK (0) or a negative PA_E* code.  On an error nothing
  *     has been enqueued.  ``pa_status_string`` gives a message; for PA_EHIP
  *     it also carries the HIP error text of the failed launch.
- *   - Device-side contents (block ids, slots, copy pairs) are trusted: the
- *     kernels do not range-check them.  Host-side sizes are checked.
+ *   - Device-side contents (block ids, slots, copy pairs, context lengths)
+ *     are trusted: the kernels do not range-check them.  Host-side sizes
+ *     are checked.  In validate mode (pa_set_validate) every call first
+ *     copies its device indices to the host and checks them.
  *   - Element types: PA_F32, PA_BF16, PA_F16.  Queries, new K/V and outputs
  *     use the pool's element type.  Arithmetic is fp32; outputs are rounded
  *     to nearest-even.
@@ -201,6 +203,19 @@ int pa_mixed_batch(const pa_kv_pool* pool, int32_t layer, void* dec_out, const v
                    void* pf_out, const void* pf_q, int32_t T, const int32_t* pf_table, int32_t pf_nb,
                    int32_t ctx_before, float scale, int32_t prefill_workgroups, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Validate mode (for debugging): when on, every call above copies the device
+ * indices it would trust to the host on its stream (synchronising it) and
+ * returns PA_EINVAL, with nothing launched, if any is wrong -- a block id
+ * outside [0, num_blocks) among a sequence's visible blocks, a context
+ * length outside [0, max_ctx] or past its table, a slot out of range or
+ * repeated, a fused append's slot that is not position context_lens - 1 of
+ * its row, a copy pair out of range or whose destination is reused.  Off by
+ * default; PA_VALIDATE=1 in the environment turns it on at load.  Not for
+ * use under graph capture.  Returns the previous setting.
+ */
+int pa_set_validate(int on);
 
 /* Message for a status code (thread-local copy of the last error detail). */
 const char* pa_status_string(int status);

@@ -46,6 +46,7 @@ SIGNATURES = {
                                         ctypes.c_size_t, _p]),
     "pa_mixed_batch": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _p, _p, _i32, _p, _i32,
                                       _i32, ctypes.c_float, _i32, _p, ctypes.c_size_t, _p]),
+    "pa_set_validate": (ctypes.c_int, [ctypes.c_int]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_bm_create": (ctypes.c_int, [_i32, _i32, _pi32, ctypes.POINTER(_p)]),
     "pa_bm_destroy": (None, [_p]),

@@ -195,6 +195,11 @@ def pa_mixed_batch(pool, layer, dec_out, dec_q, block_tables, context_lens, max_
           "pa_mixed_batch")
 
 
+def pa_set_validate(on):
+    """Validate mode on or off (returns the previous setting)."""
+    return bool(lib().pa_set_validate(1 if on else 0))
+
+
 def pa_sha256(data):
     """SHA-256 digest (32 bytes) of ``data``, computed by the library."""
     data = bytes(data)

@@ -76,6 +76,8 @@ extern "C" int pa_cache_append(const pa_kv_pool* pool, int32_t layer, const void
   const int64_t threads = 2 * chunks_per_side;
   const int64_t blocks = ceil_div(threads, 256);
   if (blocks > INT32_MAX) return fail(PA_EINVAL, "pa_cache_append: T too large for one launch");
+  if (validate_on())
+    if (int e = check_slots("pa_cache_append", pool, slot_mapping, T, stream)) return e;
   hipLaunchKernelGGL(append_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
                      static_cast<char*>(pool->k), static_cast<char*>(pool->v), static_cast<const char*>(k_new),
                      static_cast<const char*>(v_new), slot_mapping, chunks_per_side, chunks_per_row,
@@ -94,6 +96,8 @@ extern "C" int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int3
   const int32_t LH = pool->num_layers * pool->num_kv_heads;
   const int64_t wgs = static_cast<int64_t>(n) * LH * 2;
   if (wgs > INT32_MAX) return fail(PA_EINVAL, "pa_copy_blocks: too many tiles for one launch");
+  if (validate_on())
+    if (int e = check_pairs("pa_copy_blocks", pool, pairs, n, stream)) return e;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(wgs)), dim3(256), 0, stream,
                      static_cast<char*>(pool->k), static_cast<char*>(pool->v), pairs, LH, head_stride, tile_bytes);
   return check_launch("pa_copy_blocks");

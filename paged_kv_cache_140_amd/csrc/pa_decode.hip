@@ -309,6 +309,9 @@ static int decode_entry(const char* who, const pa_kv_pool* pool, int32_t layer, 
   DecodePlan pl = plan_decode(B, pool->num_kv_heads, G, pool->block_size, max_ctx);
   Workspace ws;
   if (int e = decode_workspace_check(w, pl, pool, B, H_q, workspace, workspace_bytes, &ws)) return e;
+  if (validate_on())
+    if (int e = check_decode_indices(w, pool, B, block_tables, max_blocks, context_lens, max_ctx, nt.slots, stream))
+      return e;
   const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   fn(pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens, scale_log2, pl, ws, nt, stream);
   return check_launch(who);

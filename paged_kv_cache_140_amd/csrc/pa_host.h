@@ -24,6 +24,19 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // Integer environment variable (tuning overrides), or dflt.
 int env_int(const char* name, int dflt);
 
+// ---------------------------------------------------------------- validate
+// Validate mode (pa_set_validate / PA_VALIDATE): host checks of the device
+// indices a call trusts, before it launches anything (each synchronises the
+// stream).  Each returns PA_OK or PA_EINVAL with a message.
+bool validate_on();
+int check_slots(const std::string& who, const pa_kv_pool* pool, const int32_t* slots, int32_t T, hipStream_t stream);
+int check_pairs(const std::string& who, const pa_kv_pool* pool, const int32_t* pairs, int32_t n, hipStream_t stream);
+int check_decode_indices(const std::string& who, const pa_kv_pool* pool, int32_t B, const int32_t* block_tables,
+                         int32_t max_blocks, const int32_t* context_lens, int32_t max_ctx, const int32_t* new_slots,
+                         hipStream_t stream);
+int check_prefill_indices(const std::string& who, const pa_kv_pool* pool, const int32_t* table, int32_t nb,
+                          int32_t T, int32_t ctx_before, hipStream_t stream);
+
 // ---------------------------------------------------------------- decode
 // Grid plan of a decode from host-side sizes only (context lengths stay on
 // the device): waves per workgroup, and the split of each sequence into

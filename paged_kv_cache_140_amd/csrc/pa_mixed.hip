@@ -215,6 +215,13 @@ extern "C" int pa_mixed_batch(const pa_kv_pool* pool, int32_t layer, void* dec_o
   }
   const int64_t n_dec = static_cast<int64_t>(pool->num_kv_heads) * m.pl.num_parts * B;
   if (m.n_pre + n_dec > INT32_MAX) return fail(PA_EINVAL, w + ": grid too large");
+  if (validate_on()) {
+    if (B > 0)
+      if (int e = check_decode_indices(w, pool, B, block_tables, max_blocks, context_lens, max_ctx, nullptr, stream))
+        return e;
+    if (T > 0)
+      if (int e = check_prefill_indices(w, pool, pf_table, pf_nb, T, ctx_before, stream)) return e;
+  }
   fn(pool, m, stream);
   if (B > 0 && m.pl.num_parts > 1)
     launch_decode_merge(pool->dtype, pool->head_dim, dec_out, m.ws, context_lens, B, H_q, m.pl, pool->block_size,

@@ -266,6 +266,8 @@ extern "C" int pa_prefill_chunk(const pa_kv_pool* pool, int32_t layer, void* out
       ws_ml = ws_o + static_cast<size_t>(pl.num_splits) * T * H_q * pool->head_dim;
     }
   }
+  if (validate_on())
+    if (int e = check_prefill_indices("pa_prefill_chunk", pool, block_table, nb, T, ctx_before, stream)) return e;
   const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   fn(pool, layer, out, q, T, H_q, block_table, ctx_before, scale_log2, pl, ws_o, ws_ml, stream);
   return check_launch("pa_prefill_chunk");

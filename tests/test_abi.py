@@ -39,6 +39,15 @@ def test_library_exports_every_declared_symbol():
         assert name in _lib.SIGNATURES, f"binding lacks a signature for {name}"
 
 
+def test_validate_switch():
+    from paged_kv_cache_140_amd import _lib
+
+    lib = _lib.lib()
+    old = lib.pa_set_validate(1)
+    assert lib.pa_set_validate(0) == 1
+    lib.pa_set_validate(old)
+
+
 def test_status_strings():
     from paged_kv_cache_140_amd import _lib
 
