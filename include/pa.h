@@ -119,6 +119,10 @@ size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t B, int32_t H_q, 
  *   scale: multiplies q.k before the softmax.
  *   workspace: device, at least pa_decode_workspace_size(...) bytes
  *        (may be NULL when that is 0).  Contents need no initialisation.
+ * Workgroups start in batch order.  When a batch has more (sequence, KV
+ * head) pairs than the GPU has CUs, submitting it longest context first
+ * keeps the long sequences from trailing (measured on MI355X: 8% on 64
+ * lognormal lengths with 40 KV heads, 3.5% on 63 contexts of 1k-32k).
  */
 int pa_decode(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B, int32_t H_q,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t max_ctx,

@@ -40,6 +40,8 @@ class StepInputs:
     # True when the step appends exactly one token to each decoded sequence,
     # in decode order: then append + decode can run as one pa_decode_append.
     fusable: bool = False
+    # launch row i of the decode holds the step's decode row order[i]
+    order: object = None
 
 
 class GpuRun:
@@ -99,9 +101,17 @@ class GpuRun:
                 raise ValueError(op)
 
     # -- one step ------------------------------------------------------------
-    def prepare(self, step):
+    def prepare(self, step, longest_first=False):
         """Host bookkeeping for ``step`` (its forks and frees, then its
-        appends) and H2D staging of all its inputs."""
+        appends) and H2D staging of all its inputs.
+
+        ``longest_first``: submit the decode batch longest context first, as
+        a scheduler can (the decode starts its workgroups in batch order;
+        when they outnumber the CUs, the long ones then do not trail).  The
+        bookkeeping stays in the step's order; only the decode's launch rows
+        (tables, lengths, queries and, for a fused step, the new tokens and
+        their slots) are permuted, and ``si.order[i]`` is the step row that
+        launch row i holds."""
         cfg, dev = self.cfg, self.device
         for op in step.ops:
             if op[0] == "fork":
@@ -132,6 +142,15 @@ class GpuRun:
             si.out = torch.empty_like(si.q)
             si.workspace = decode_workspace(self.pool, len(step.decode_seqs), cfg["H_q"], max_ctx, dev)
             si.fusable = list(step.appends) == [(s_, 1) for s_ in step.decode_seqs]
+            si.order = np.arange(len(lens))
+            if longest_first:
+                perm = np.argsort(-lens, kind="stable")
+                pt = torch.from_numpy(perm).to(dev)
+                si.order = perm
+                si.tables, si.lens, si.q = si.tables[pt].contiguous(), si.lens[pt].contiguous(), si.q[pt].contiguous()
+                if si.fusable:
+                    si.k_new, si.v_new = si.k_new[pt].contiguous(), si.v_new[pt].contiguous()
+                    si.slots = si.slots[pt].contiguous()
         if step.prefill is not None:
             pf = step.prefill
             table = np.array(self.bm.block_table(pf.seq), dtype=np.int32)
@@ -172,7 +191,7 @@ class GpuRun:
             q, table, ctx_before, out, ws = si.prefill
             pa_prefill_chunk(self.pool, self.layer, out, q, table, ctx_before, cfg["scale"], ws, stream)
 
-    def run_step(self, step, fused=False):
-        si = self.prepare(step)
+    def run_step(self, step, fused=False, longest_first=False):
+        si = self.prepare(step, longest_first=longest_first)
         self.launch(si, fused=fused)
         return si
