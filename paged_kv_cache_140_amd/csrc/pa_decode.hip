@@ -48,13 +48,22 @@ __global__ void __launch_bounds__(MAXT)
                   const char* __restrict__ k_new, const char* __restrict__ v_new,
                   const int32_t* __restrict__ new_slots) {
   extern __shared__ float smem[];
-  // Grid (kv head, partition, sequence), kv head fastest: workgroup i runs on
-  // XCD i % 8, so with H_kv a multiple of 8 every XCD gets the same heads of
-  // every partition of every sequence -- the same bytes.  With the partition
-  // fastest, a partition count that is a multiple of 8 would put every
-  // sequence's first partition (always present) on one XCD and the late ones
-  // (long sequences only) on another.
-  decode_body<E, D, G, BS, FUSED>(blockIdx.x, blockIdx.y, gridDim.x, blockIdx.z, smem, pool_k, pool_v, layer_off,
+  // Grid (kv head, partition slot, sequence), kv head fastest: workgroup i
+  // runs on XCD i % 8, so with H_kv a multiple of 8 every XCD gets the same
+  // heads of every partition of every sequence -- the same bytes.  Inside an
+  // XCD the workgroups are dealt round its CUs in turn, so one partition per
+  // slot would, with a partition count that is a multiple of 4, give some
+  // CUs every sequence's first partition (always present) and others only
+  // the late ones of long sequences; rotating the partition by the low bits
+  // of the sequence index spreads them.  (Measured on 63 contexts of
+  // 1k-32k: 4 / 8 / 16 partitions 1,023 / 895 / 863 us unrotated, 788 /
+  // 787 / 819 us rotated.)  Fewer than 4 partitions: no rotation, no cost.
+  int part = blockIdx.y;
+  if (num_parts >= 4) {
+    part += blockIdx.z & 3;
+    if (part >= num_parts) part -= num_parts;
+  }
+  decode_body<E, D, G, BS, FUSED>(blockIdx.x, part, gridDim.x, blockIdx.z, smem, pool_k, pool_v, layer_off,
                                   head_stride, q, out, block_tables, max_blocks, context_lens, scale_log2, H_q,
                                   blocks_per_part, num_parts, ws_ml, ws_acc, k_new, v_new, new_slots);
 }

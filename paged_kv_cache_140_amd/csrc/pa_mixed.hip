@@ -68,10 +68,19 @@ __global__ void __launch_bounds__(kPrefillThreads)
     }
     return;
   }
+  // decode workgroups in the decode kernel's order: kv head fastest, then
+  // the partition slot (rotated as there by the sequence index's low bits),
+  // then the sequence
   const int j = id - n_pre;
   const int g = j % H_kv;
   const int rest = j / H_kv;
-  decode_body<E, D, G, BS, false>(g, rest % num_parts, H_kv, rest / num_parts, reinterpret_cast<float*>(&lds[0][0]),
+  const int b = rest / num_parts;
+  int part = rest % num_parts;
+  if (num_parts >= 4) {
+    part += b & 3;
+    if (part >= num_parts) part -= num_parts;
+  }
+  decode_body<E, D, G, BS, false>(g, part, H_kv, b, reinterpret_cast<float*>(&lds[0][0]),
                                   pool_k, pool_v, layer_off, head_stride, dq, dout, block_tables, max_blocks,
                                   context_lens, scale_log2, H_q, blocks_per_part, num_parts, ws_ml, ws_acc, nullptr,
                                   nullptr, nullptr);
