@@ -74,7 +74,7 @@ def write_traffic_record(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
     import statistics
 
     def per_dispatch(d, counter):
-        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        path = max(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True), key=os.path.getmtime)
         acc, names = {}, {}
         with open(path) as f:
             for r in csv.DictReader(f):
