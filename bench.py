@@ -385,6 +385,7 @@ def main():
                                "speedup": round(ms_sep / ms_mix, 3),
                                "GBps": round(decode_bytes(L5, 8, 64, 128, 16, 2) / (ms_mix * 1e-3) / 1e9, 1),
                                "TFLOPs": round(fl / (ms_mix * 1e-3) / 1e12, 1)}
+        rows["mixed_batch_4_chunks"] = four_chunk_row(torch, pa, np, g5, s5, fl)
         del g5, s5
         torch.cuda.empty_cache()
         rows["prefix_cache"] = prefix_cache_row(torch, pa, np)
@@ -397,6 +398,44 @@ def main():
     out["wall_s"] = round(time.time() - t_start, 1)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def four_chunk_row(torch, pa, np, g5, s5, fl_one):
+    """The 63 long-context decodes with four 256-row prefill chunks of
+    different sequences (after 200, 1,000, 3,500 and 8,000 cached tokens) in
+    one pa_mixed_batch, against pa_decode + four pa_prefill_chunk calls."""
+    cfg = g5.cfg
+    H_q, d = cfg["H_q"], cfg["d"]
+    chunks = [(256, 200), (256, 1000), (256, 3500), (256, 8000)]
+    tables = []
+    for i, (T, cb) in enumerate(chunks):
+        seq = 500000 + i
+        g5.bm.add_seq(seq)
+        g5.bm.append_slots(seq, cb + T)  # the pool already holds N(0,1) K/V everywhere
+        tables.append(g5.bm.block_table(seq))
+    width = max(len(t) for t in tables)
+    pt = torch.tensor([t + [0] * (width - len(t)) for t in tables], dtype=torch.int32, device="cuda")
+    pq = torch.randn(sum(T for T, _ in chunks), H_q, d, device="cuda").to(torch.bfloat16)
+    pout = torch.empty_like(pq)
+    rows0 = np.cumsum([0] + [T for T, _ in chunks])
+
+    def separate(i):
+        g5.launch(s5, do_copy=False, do_append=False, do_prefill=False)
+        for c, (T, cb) in enumerate(chunks):
+            r = slice(int(rows0[c]), int(rows0[c + 1]))
+            pa.pa_prefill_chunk(g5.pool, 0, pout[r], pq[r], pt[c], cb, cfg["scale"])
+
+    def mixed(i):
+        pa.pa_mixed_batch(g5.pool, 0, s5.out, s5.q, s5.tables, s5.lens, s5.max_ctx, pout, pq, chunks, pt,
+                          cfg["scale"], 0, s5.workspace)
+
+    ms_sep = time_loop(torch, separate, 10, 2)
+    ms_mix = time_loop(torch, mixed, 10, 2)
+    flops = sum(prefill_flops(T, H_q, d, cb) for T, cb in chunks)
+    return {"workload": "the 63 decodes (longest first) + 4 chunks of 256 rows after 200 / 1,000 / 3,500 / 8,000 "
+                        "cached tokens, GQA 64/8, as one pa_mixed_batch",
+            "ms": round(ms_mix, 5), "separate_ms": round(ms_sep, 5), "speedup": round(ms_sep / ms_mix, 3),
+            "prefill_GFLOP": round(flops / 1e9, 1)}
 
 
 def capacity_row(pa, np):

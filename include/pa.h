@@ -179,34 +179,44 @@ int pa_prefill_chunk(const pa_kv_pool* pool, int32_t layer, void* out, const voi
                      size_t workspace_bytes, hipStream_t stream);
 
 /*
- * A mixed batch in one launch: the decode step of B sequences and one causal
- * prefill chunk of another sequence.  Chunked prefill lets the running
- * requests' decode steps share a step with a piece of a long prompt, so
- * that the prompt does not stall them ([ttlab] "새 문제: 긴 프리필이 디코드를
- * 멈춘다").  Same results as pa_decode(pool, layer, dec_out, dec_q, B, H_q,
- * block_tables, max_blocks, context_lens, max_ctx, scale, workspace, ...)
- * followed by pa_prefill_chunk(pool, layer, pf_out, pf_q, T, H_q, pf_table,
- * pf_nb, ctx_before, scale, ...): bit for bit, since both halves run the
- * same per-workgroup code.  The decode half streams K/V from HBM while the
- * chunk's tiles run on the matrix cores of prefill_workgroups CUs.
+ * A mixed batch in one launch: the decode step of B sequences and the causal
+ * prefill chunks of others.  Chunked prefill lets the running requests'
+ * decode steps share a step with pieces of long prompts, so that the prompts
+ * do not stall them ([ttlab] "새 문제: 긴 프리필이 디코드를 멈춘다").  Same
+ * results as pa_decode(pool, layer, dec_out, dec_q, B, H_q, block_tables,
+ * max_blocks, context_lens, max_ctx, scale, workspace, ...) followed by, for
+ * each chunk c, pa_prefill_chunk(pool, layer, its rows of pf_out, its rows
+ * of pf_q, chunks[c].T, H_q, row c of pf_tables, pf_max_blocks,
+ * chunks[c].ctx_before, scale, NULL, 0, ...): bit for bit, since both halves
+ * run the same per-workgroup code.  The decode half streams K/V from HBM
+ * while the chunks' tiles run on the matrix cores of prefill_workgroups CUs.
  *   Decode arguments: as pa_decode (B may be 0).
- *   Prefill arguments: as pa_prefill_chunk (T may be 0).  The chunk's
- *        sequence must not be one of the decoded ones, and its K/V must
- *        already be appended.
- *   prefill_workgroups: persistent workgroups that share the chunk's
+ *   pf_q, pf_out: device [sum of T][H_q][head_dim], the chunks' rows packed
+ *        in chunk order.
+ *   chunks: host [n_chunks], 0 <= n_chunks <= 32; a chunk may have T = 0.
+ *        The chunks' sequences must not be decoded in the same call, and
+ *        their own K/V must already be appended.
+ *   pf_tables: device int32 [n_chunks][pf_max_blocks]; row c is chunk c's
+ *        block table, pf_max_blocks >= ceil((ctx_before + T) / block_size).
+ *   prefill_workgroups: persistent workgroups that share the chunks'
  *        (position tile, KV head) items, longest first; 0 lets the library
- *        pick (a number that should let the chunk end before the decode).
+ *        pick (a number that should let the chunks end before the decode).
  *        More than the number of items is clamped to it.
  *   workspace: as pa_decode, for the decode half (pa_decode_workspace_size).
  *   bf16 and f16 pools only.  The decode half runs 8 waves per workgroup
  *   whatever PA_DECODE_WAVES says.  A split decode adds a second, small
  *   launch (the partition merge), as in pa_decode.
  */
+typedef struct pa_chunk {
+  int32_t T;          /* rows of the chunk */
+  int32_t ctx_before; /* tokens of its sequence before the chunk */
+} pa_chunk;
+
 int pa_mixed_batch(const pa_kv_pool* pool, int32_t layer, void* dec_out, const void* dec_q, int32_t B, int32_t H_q,
                    const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t max_ctx,
-                   void* pf_out, const void* pf_q, int32_t T, const int32_t* pf_table, int32_t pf_nb,
-                   int32_t ctx_before, float scale, int32_t prefill_workgroups, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream);
+                   void* pf_out, const void* pf_q, const pa_chunk* chunks, int32_t n_chunks,
+                   const int32_t* pf_tables, int32_t pf_max_blocks, float scale, int32_t prefill_workgroups,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Validate mode (for debugging): when on, every call above copies the device

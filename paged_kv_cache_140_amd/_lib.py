@@ -33,6 +33,10 @@ class KVPoolStruct(ctypes.Structure):
 
 _PPOOL = ctypes.POINTER(KVPoolStruct)
 
+
+class ChunkStruct(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("ctx_before", ctypes.c_int32)]
+
 SIGNATURES = {
     "pa_cache_append": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _p, _i32, _p]),
     "pa_copy_blocks": (ctypes.c_int, [_PPOOL, _p, _i32, _p]),
@@ -44,8 +48,9 @@ SIGNATURES = {
     "pa_prefill_workspace_size": (ctypes.c_size_t, [_PPOOL, _i32, _i32, _i32]),
     "pa_prefill_chunk": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _i32, ctypes.c_float, _p,
                                         ctypes.c_size_t, _p]),
-    "pa_mixed_batch": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _p, _p, _i32, _p, _i32,
-                                      _i32, ctypes.c_float, _i32, _p, ctypes.c_size_t, _p]),
+    "pa_mixed_batch": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _p, _p,
+                                      ctypes.POINTER(ChunkStruct), _i32, _p, _i32, ctypes.c_float, _i32, _p,
+                                      ctypes.c_size_t, _p]),
     "pa_set_validate": (ctypes.c_int, [ctypes.c_int]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_bm_create": (ctypes.c_int, [_i32, _i32, _pi32, ctypes.POINTER(_p)]),

@@ -165,32 +165,36 @@ def pa_prefill_chunk(pool, layer, out, q, block_table, ctx_before, scale, worksp
                                  _stream(stream)), "pa_prefill_chunk")
 
 
-def pa_mixed_batch(pool, layer, dec_out, dec_q, block_tables, context_lens, max_ctx, pf_out, pf_q, pf_table,
-                   ctx_before, scale, prefill_workgroups=0, workspace=None, stream=None):
-    """A decode batch (as pa_decode) and one prefill chunk (as
-    pa_prefill_chunk) in one launch.  dec_q may have B = 0 rows and pf_q
-    T = 0 rows."""
+def pa_mixed_batch(pool, layer, dec_out, dec_q, block_tables, context_lens, max_ctx, pf_out, pf_q, chunks,
+                   pf_tables, scale, prefill_workgroups=0, workspace=None, stream=None):
+    """A decode batch (as pa_decode) and prefill chunks (as pa_prefill_chunk
+    each) in one launch.  dec_q may have B = 0 rows.  chunks: list of
+    (T, ctx_before); their rows are packed in order in pf_q / pf_out
+    ([sum T][H_q][d]); pf_tables: int32 [len(chunks)][max_blocks], row c the
+    block table of chunk c."""
     B, H_q, _ = (int(x) for x in dec_q.shape)
-    T = int(pf_q.shape[0])
+    chunks = [(int(t), int(c)) for t, c in chunks]
+    rows = sum(t for t, _ in chunks)
     _need(dec_q, "dec_q", pool.torch_dtype, (B, H_q, pool.head_dim))
     _need(dec_out, "dec_out", pool.torch_dtype, (B, H_q, pool.head_dim))
     _need(block_tables, "block_tables", torch.int32)
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [B][max_blocks]")
     _need(context_lens, "context_lens", torch.int32, (B,))
-    _need(pf_q, "pf_q", pool.torch_dtype, (T, H_q, pool.head_dim))
-    _need(pf_out, "pf_out", pool.torch_dtype, (T, H_q, pool.head_dim))
-    _need(pf_table, "pf_table", torch.int32)
-    if pf_table.dim() != 1:
-        raise ValueError("pf_table must be 1-D")
+    _need(pf_q, "pf_q", pool.torch_dtype, (rows, H_q, pool.head_dim))
+    _need(pf_out, "pf_out", pool.torch_dtype, (rows, H_q, pool.head_dim))
+    _need(pf_tables, "pf_tables", torch.int32)
+    if pf_tables.dim() != 2 or pf_tables.shape[0] != len(chunks):
+        raise ValueError("pf_tables must be [n_chunks][max_blocks]")
     ws_bytes = 0
     if workspace is not None:
         _need(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
+    arr = (_lib.ChunkStruct * max(len(chunks), 1))(*[_lib.ChunkStruct(t, c) for t, c in chunks])
     s = pool.struct()
     check(lib().pa_mixed_batch(ctypes.byref(s), layer, _ptr(dec_out), _ptr(dec_q), B, H_q, _ptr(block_tables),
                                int(block_tables.shape[1]), _ptr(context_lens), int(max_ctx), _ptr(pf_out),
-                               _ptr(pf_q), T, _ptr(pf_table), int(pf_table.shape[0]), int(ctx_before), float(scale),
+                               _ptr(pf_q), arr, len(chunks), _ptr(pf_tables), int(pf_tables.shape[1]), float(scale),
                                int(prefill_workgroups), _ptr(workspace), ws_bytes, _stream(stream)),
           "pa_mixed_batch")
 

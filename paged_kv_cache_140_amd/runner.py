@@ -173,8 +173,9 @@ class GpuRun:
             if do_append and si.slots.numel():
                 pa_cache_append(self.pool, self.layer, si.k_new, si.v_new, si.slots, stream)
             q, table, ctx_before, out, _ = si.prefill
-            pa_mixed_batch(self.pool, self.layer, si.out, si.q, si.tables, si.lens, si.max_ctx, out, q, table,
-                           ctx_before, cfg["scale"], prefill_workgroups, si.workspace, stream)
+            pa_mixed_batch(self.pool, self.layer, si.out, si.q, si.tables, si.lens, si.max_ctx, out, q,
+                           [(q.shape[0], ctx_before)], table.view(1, -1), cfg["scale"], prefill_workgroups,
+                           si.workspace, stream)
             return
         if do_copy and si.n_pairs:
             pa_copy_blocks(self.pool, si.pairs, stream)

@@ -87,10 +87,13 @@ def test_host_side_argument_checks_need_no_gpu():
                                 None, 0, None) == _lib.PA_OK
     # mixed batch: both halves empty; H_q not a multiple of H_kv; chunk table too short; negative
     # prefill workgroups; an f32 pool (no matrix-core path)
-    def mixed(B, H_q, T, nb=8, n_pre=0):
-        return lib.pa_mixed_batch(ctypes.byref(pool), 0, 256, 256, B, H_q, 256, 64, 256, 100, 256, 256, T, 256, nb,
-                                  100, 0.1, n_pre, None, 0, None)
+    def mixed(B, H_q, T, nb=8, n_pre=0, n_chunks=1):
+        ch = (_lib.ChunkStruct * 40)(*[_lib.ChunkStruct(T, 100) for _ in range(40)])
+        return lib.pa_mixed_batch(ctypes.byref(pool), 0, 256, 256, B, H_q, 256, 64, 256, 100, 256, 256, ch, n_chunks,
+                                  256, nb, 0.1, n_pre, None, 0, None)
     assert mixed(0, 16, 0) == _lib.PA_OK
+    assert mixed(0, 16, 0, n_chunks=0) == _lib.PA_OK
+    assert mixed(0, 16, 0, n_chunks=33) == _lib.PA_EINVAL  # at most 32 chunks per launch
     assert mixed(2, 12, 0) == _lib.PA_EINVAL
     assert mixed(0, 16, 100, nb=12) == _lib.PA_EINVAL  # (100 + 100) / 16 -> 13 blocks needed
     assert mixed(0, 16, 100, nb=13, n_pre=-1) == _lib.PA_EINVAL

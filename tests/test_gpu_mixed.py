@@ -1,6 +1,6 @@
-"""pa_mixed_batch -- a decode batch and one causal prefill chunk in one
-launch -- against the oracle, and bit for bit against pa_decode followed by
-pa_prefill_chunk on the same inputs."""
+"""pa_mixed_batch -- a decode batch and causal prefill chunks in one launch
+-- against the oracle, and bit for bit against pa_decode followed by one
+pa_prefill_chunk per chunk on the same inputs."""
 
 import numpy as np
 import pytest
@@ -16,12 +16,13 @@ from pa_inputs import build_scenario
 pytestmark = pytest.mark.gpu
 
 
-def _world(rng, dec_lengths, chunk_total, H_kv, d, bs, dtype):
-    """Decode sequences 0..B-1 and the chunk's sequence B in one NaN-poisoned
-    pool with a scattered free order; the same bits on the GPU."""
+def _world(rng, dec_lengths, chunk_totals, H_kv, d, bs, dtype):
+    """Decode sequences 0..B-1 and one sequence per prefill chunk after them,
+    in one NaN-poisoned pool with a scattered free order; the same bits on
+    the GPU."""
     from paged_kv_cache_140_amd import KVPool
 
-    lengths = list(dec_lengths) + [chunk_total]
+    lengths = list(dec_lengths) + list(chunk_totals)
     N = sum(-(-n // bs) for n in lengths) + 13
     bm = OracleBM(N, bs, rng.permutation(N))
     op = Pool(1, H_kv, N, bs, d, dtype)
@@ -40,16 +41,19 @@ def _world(rng, dec_lengths, chunk_total, H_kv, d, bs, dtype):
 
 
 class _Batch:
-    """Device inputs of one mixed batch and helpers that run it either way."""
+    """Device inputs of one mixed batch -- decode rows and prefill chunks
+    (ctx_before, T), the chunks' rows packed in order -- and helpers that run
+    it either way."""
 
-    def __init__(self, gp, tables, dec_lengths, ctx_before, T, H_q, d, dtype, rng):
+    def __init__(self, gp, tables, dec_lengths, chunks, H_q, d, dtype, rng):
         from paged_kv_cache_140_amd import decode_workspace
         from paged_kv_cache_140_amd.runner import to_device
 
         B = len(dec_lengths)
-        self.gp, self.dtype = gp, dtype
+        self.gp, self.dtype, self.chunks = gp, dtype, list(chunks)
+        rows = sum(t for _, t in chunks)
         self.dq32 = rng.standard_normal((B, H_q, d)).astype(np.float32)
-        self.pq32 = rng.standard_normal((T, H_q, d)).astype(np.float32)
+        self.pq32 = rng.standard_normal((rows, H_q, d)).astype(np.float32)
         self.dq = to_device(self.dq32, dtype, "cuda")
         self.pq = to_device(self.pq32, dtype, "cuda")
         maxb = max([len(t) for t in tables[:B]] + [1])
@@ -59,8 +63,15 @@ class _Batch:
         self.tab = torch.from_numpy(tab).cuda()
         self.lens = torch.tensor(dec_lengths, dtype=torch.int32).cuda()
         self.max_ctx = max(list(dec_lengths) + [0])
-        self.ptab = torch.tensor(tables[B] + [0, 0], dtype=torch.int32).cuda()
-        self.ctx_before = ctx_before
+        ctabs = tables[B:]
+        pmax = max([len(t) for t in ctabs] + [1]) + 2
+        pt = np.zeros((len(chunks), pmax), dtype=np.int32)
+        for c, t in enumerate(ctabs):
+            pt[c, :len(t)] = t
+        self.ctables = ctabs
+        self.dtables = tables[:B]
+        self.ptabs = torch.from_numpy(pt).cuda()
+        self.row0 = np.cumsum([0] + [t for _, t in chunks])
         self.scale = float(np.float32(1 / np.sqrt(d)))
         self.ws = decode_workspace(gp, B, H_q, self.max_ctx) if B else None
 
@@ -73,8 +84,10 @@ class _Batch:
         dout, pout = self.outs()
         if self.dq.shape[0]:
             pa_decode(self.gp, 0, dout, self.dq, self.tab, self.lens, self.max_ctx, self.scale, self.ws)
-        if self.pq.shape[0]:
-            pa_prefill_chunk(self.gp, 0, pout, self.pq, self.ptab, self.ctx_before, self.scale)
+        for c, (ctx_before, T) in enumerate(self.chunks):
+            if T:
+                r = slice(int(self.row0[c]), int(self.row0[c + 1]))
+                pa_prefill_chunk(self.gp, 0, pout[r], self.pq[r], self.ptabs[c], ctx_before, self.scale)
         torch.cuda.synchronize()
         return dout, pout
 
@@ -82,34 +95,53 @@ class _Batch:
         from paged_kv_cache_140_amd import pa_mixed_batch
 
         dout, pout = self.outs()
-        pa_mixed_batch(self.gp, 0, dout, self.dq, self.tab, self.lens, self.max_ctx, pout, self.pq, self.ptab,
-                       self.ctx_before, self.scale, n_pre, self.ws)
+        pa_mixed_batch(self.gp, 0, dout, self.dq, self.tab, self.lens, self.max_ctx, pout, self.pq,
+                       [(T, cb) for cb, T in self.chunks], self.ptabs, self.scale, n_pre, self.ws)
         torch.cuda.synchronize()
         return dout, pout
 
+    def oracle(self, op, dec_lengths):
+        """The oracle's decode rows and chunk rows (packed like pf_out)."""
+        dref = (attention.decode(op, 0, widen(self.dq32, self.dtype), self.dtables, list(dec_lengths), self.scale)
+                if len(dec_lengths) else np.zeros(self.dq32.shape))
+        pq = widen(self.pq32, self.dtype)
+        pref = np.zeros(pq.shape)
+        for c, (ctx_before, T) in enumerate(self.chunks):
+            if T:
+                r = slice(int(self.row0[c]), int(self.row0[c + 1]))
+                pref[r] = attention.prefill_chunk(op, 0, pq[r], self.ctables[c], ctx_before, self.scale)
+        return dref, pref
+
 
 CASES = [
-    # H_q, H_kv, d, bs, dtype, decode lengths, ctx_before, T
-    (64, 8, 128, 16, "bf16", [1, 17, 640, 1000, 3000], 500, 300),
-    (16, 8, 128, 16, "bf16", [2, 33, 600], 0, 33),
-    (8, 8, 64, 8, "bf16", [9, 100, 0, 257], 37, 129),
-    (32, 8, 64, 32, "f16", [5, 64, 65, 3000], 64, 64),
-    (16, 4, 64, 16, "f16", [15, 16, 250], 250, 77),
-    (4, 1, 128, 32, "f16", [3, 4097], 1, 1),
-    (8, 2, 128, 16, "bf16", [31, 32, 1024], 1000, 17),
+    # H_q, H_kv, d, bs, dtype, decode lengths, chunks as (ctx_before, T)
+    (64, 8, 128, 16, "bf16", [1, 17, 640, 1000, 3000], [(500, 300)]),
+    (16, 8, 128, 16, "bf16", [2, 33, 600], [(0, 33)]),
+    (8, 8, 64, 8, "bf16", [9, 100, 0, 257], [(37, 129)]),
+    (32, 8, 64, 32, "f16", [5, 64, 65, 3000], [(64, 64)]),
+    (16, 4, 64, 16, "f16", [15, 16, 250], [(250, 77)]),
+    (4, 1, 128, 32, "f16", [3, 4097], [(1, 1)]),
+    (8, 2, 128, 16, "bf16", [31, 32, 1024], [(1000, 17)]),
+    # several chunks of different lengths after different contexts, one empty
+    (64, 8, 128, 16, "bf16", [70, 1500], [(300, 200), (0, 0), (2000, 33), (40, 257)]),
+    (16, 8, 128, 16, "bf16", [5, 900, 31], [(10, 5), (700, 64), (1200, 300)]),
+    (32, 8, 64, 8, "f16", [], [(100 * i, 20 + 7 * i) for i in range(8)]),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"{c[4]}-hq{c[0]}-hkv{c[1]}-d{c[2]}-bs{c[3]}-c{c[6]}-t{c[7]}"
-                                             for c in CASES])
+def _ids(c):
+    ch = "+".join(f"{cb}:{t}" for cb, t in c[6])
+    return f"{c[4]}-hq{c[0]}-hkv{c[1]}-d{c[2]}-bs{c[3]}-chunks{ch}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
 def test_mixed_batch_matches_oracle_and_separate_calls(case):
-    H_q, H_kv, d, bs, dtype, dec_lengths, ctx_before, T = case
-    rng = np.random.default_rng(sum(dec_lengths) + 7 * T + d)
+    H_q, H_kv, d, bs, dtype, dec_lengths, chunks = case
+    rng = np.random.default_rng(sum(dec_lengths) + 7 * sum(t for _, t in chunks) + d)
     say("mixed", case)
-    op, gp, tables = _world(rng, dec_lengths, ctx_before + T, H_kv, d, bs, dtype)
-    b = _Batch(gp, tables, dec_lengths, ctx_before, T, H_q, d, dtype, rng)
-    dref = attention.decode(op, 0, widen(b.dq32, dtype), tables[:len(dec_lengths)], dec_lengths, b.scale)
-    pref = attention.prefill_chunk(op, 0, widen(b.pq32, dtype), tables[-1], ctx_before, b.scale)
+    op, gp, tables = _world(rng, dec_lengths, [cb + t for cb, t in chunks], H_kv, d, bs, dtype)
+    b = _Batch(gp, tables, dec_lengths, chunks, H_q, d, dtype, rng)
+    dref, pref = b.oracle(op, dec_lengths)
     sep_d, sep_p = b.separate()
     for n_pre in (0, 1, 3, 8, 1000):
         say("  prefill workgroups", n_pre)
@@ -128,12 +160,12 @@ def test_mixed_batch_split_decode(part_blocks, monkeypatch):
     monkeypatch.setenv("PA_DECODE_PART_BLOCKS", str(part_blocks))
     H_q, H_kv, d, bs, dtype = 64, 8, 128, 16, "bf16"
     dec_lengths = [1, 300, 2049, 5000]
+    chunks = [(700, 200), (90, 31)]
     rng = np.random.default_rng(part_blocks)
     say("mixed split", part_blocks)
-    op, gp, tables = _world(rng, dec_lengths, 700 + 200, H_kv, d, bs, dtype)
-    b = _Batch(gp, tables, dec_lengths, 700, 200, H_q, d, dtype, rng)
-    dref = attention.decode(op, 0, widen(b.dq32, dtype), tables[:4], dec_lengths, b.scale)
-    pref = attention.prefill_chunk(op, 0, widen(b.pq32, dtype), tables[-1], 700, b.scale)
+    op, gp, tables = _world(rng, dec_lengths, [cb + t for cb, t in chunks], H_kv, d, bs, dtype)
+    b = _Batch(gp, tables, dec_lengths, chunks, H_q, d, dtype, rng)
+    dref, pref = b.oracle(op, dec_lengths)
     sep_d, sep_p = b.separate()
     for n_pre in (0, 16):
         md, mp = b.mixed(n_pre)
@@ -143,23 +175,22 @@ def test_mixed_batch_split_decode(part_blocks, monkeypatch):
         assert np.array_equal(bits(mp), bits(sep_p))
 
 
-@pytest.mark.parametrize("which", ["prefill_only", "decode_only"])
+@pytest.mark.parametrize("which", ["prefill_only", "decode_only", "no_chunks"])
 def test_mixed_batch_one_half_empty(which):
     H_q, H_kv, d, bs, dtype = 16, 8, 128, 16, "bf16"
     dec_lengths = [] if which == "prefill_only" else [5, 77, 1500]
-    T = 100 if which == "prefill_only" else 0
+    chunks = {"prefill_only": [(400, 100)], "decode_only": [(400, 0)], "no_chunks": []}[which]
     rng = np.random.default_rng(len(which))
     say("mixed", which)
-    op, gp, tables = _world(rng, dec_lengths, 400 + T, H_kv, d, bs, dtype)
-    b = _Batch(gp, tables, dec_lengths, 400, T, H_q, d, dtype, rng)
+    op, gp, tables = _world(rng, dec_lengths, [cb + t for cb, t in chunks], H_kv, d, bs, dtype)
+    b = _Batch(gp, tables, dec_lengths, chunks, H_q, d, dtype, rng)
     sep_d, sep_p = b.separate()
     md, mp = b.mixed(0)
     assert np.array_equal(bits(md), bits(sep_d)) and np.array_equal(bits(mp), bits(sep_p))
+    dref, pref = b.oracle(op, dec_lengths)
     if dec_lengths:
-        dref = attention.decode(op, 0, widen(b.dq32, dtype), tables[:len(dec_lengths)], dec_lengths, b.scale)
         assert max_abs_err(f64(md), dref) <= TOL[dtype]
-    else:
-        pref = attention.prefill_chunk(op, 0, widen(b.pq32, dtype), tables[-1], 400, b.scale)
+    if sum(t for _, t in chunks):
         assert max_abs_err(f64(mp), pref) <= TOL[dtype]
 
 

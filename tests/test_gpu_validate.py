@@ -82,8 +82,11 @@ def test_validate_rejects_bad_indices_before_launch(world):
     pbad = ptab.clone()
     pbad[4] = N + 1
     _expect_einval(pa_prefill_chunk, pool, 0, pout, pq, pbad, 100, 0.1)
-    _expect_einval(pa_mixed_batch, pool, 0, out, q, bad, lens, 64, pout, pq, ptab, 100, 0.1, 0,
-                   decode_workspace(pool, 2, H_Q, 64))
+    ws = decode_workspace(pool, 2, H_Q, 64)
+    _expect_einval(pa_mixed_batch, pool, 0, out, q, bad, lens, 64, pout, pq, [(40, 100)], ptab.view(1, -1), 0.1, 0,
+                   ws)
+    _expect_einval(pa_mixed_batch, pool, 0, out, q, tab, lens, 64, pout, pq, [(40, 100)], pbad.view(1, -1), 0.1, 0,
+                   ws)
     torch.cuda.synchronize()
     assert torch.isnan(pout.float()).all() and torch.isnan(out.float()).all()
 
