@@ -56,7 +56,8 @@ enum {
  * reads K/V by layer, KV head, token and head dimension ([icarus] "类比的边界").
  *
  * k, v: device, each [num_layers][num_kv_heads][num_blocks][block_size][head_dim]
- * row-major, element type ``dtype``.  One block of one head is a contiguous
+ * row-major, element type ``dtype``, 16-byte aligned (every call returns
+ * PA_EINVAL otherwise).  One block of one head is a contiguous
  * block_size * head_dim run (4 KiB for 16 x 128 bf16).  Slot s of a layer and
  * head is token s % block_size of block s / block_size.
  */
@@ -74,7 +75,8 @@ typedef struct pa_kv_pool {
 /*
  * Append: write each new token's K/V into its slot of the current block
  * ([icarus] "Block Table 如何工作"; [ttlab] "블록과 블록 표").
- *   k_new, v_new: device [T][num_kv_heads][head_dim], pool dtype.
+ *   k_new, v_new: device [T][num_kv_heads][head_dim], pool dtype, 16-byte
+ *                 aligned.
  *   slot_mapping: device int32 [T]; a negative slot skips that row.  Slots
  *                 must be distinct and < num_blocks * block_size.
  *   T >= 0 (T == 0 enqueues nothing).

@@ -68,6 +68,8 @@ extern "C" int pa_cache_append(const pa_kv_pool* pool, int32_t layer, const void
   if (T < 0) return fail(PA_EINVAL, "pa_cache_append: T < 0");
   if (T == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping) return fail(PA_EINVAL, "pa_cache_append: NULL input");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_EINVAL, "pa_cache_append: k_new and v_new must be 16-byte aligned");
   const int64_t row_bytes = static_cast<int64_t>(pool->head_dim) * elem_bytes(pool->dtype);
   const int32_t chunks_per_row = static_cast<int32_t>(row_bytes / 16);
   const int64_t chunks_per_side = static_cast<int64_t>(T) * pool->num_kv_heads * chunks_per_row;

@@ -25,6 +25,7 @@ int check_launch(const char* what) {
 int check_pool(const pa_kv_pool* pool, int32_t layer) {
   if (!pool) return fail(PA_EINVAL, "pool is NULL");
   if (!pool->k || !pool->v) return fail(PA_EINVAL, "pool k/v pointer is NULL");
+  if (!aligned16(pool->k) || !aligned16(pool->v)) return fail(PA_EINVAL, "pool k and v must be 16-byte aligned");
   if (pool->num_layers <= 0 || pool->num_kv_heads <= 0 || pool->num_blocks <= 0 || pool->block_size <= 0 ||
       pool->head_dim <= 0)
     return fail(PA_EINVAL, "pool sizes must be positive");

@@ -100,6 +100,15 @@ def test_host_side_argument_checks_need_no_gpu():
     pool.dtype = _lib.PA_F32
     assert mixed(2, 16, 0) == _lib.PA_ENOTSUP
     pool.dtype = _lib.PA_BF16
+    # 16-byte alignment of the pool and of the appended rows (the kernels move 16-byte chunks)
+    assert lib.pa_cache_append(ctypes.byref(pool), 0, 264, 256, 256, 4, None) == _lib.PA_EINVAL
+    assert lib.pa_cache_append(ctypes.byref(pool), 0, 256, 258, 256, 4, None) == _lib.PA_EINVAL
+    pool.v = 264
+    assert lib.pa_cache_append(ctypes.byref(pool), 0, 256, 256, 256, 4, None) == _lib.PA_EINVAL
+    assert lib.pa_copy_blocks(ctypes.byref(pool), 256, 1, None) == _lib.PA_EINVAL
+    assert lib.pa_decode(ctypes.byref(pool), 0, 256, 256, 2, 16, 256, 64, 256, 100, 0.1, None, 0, None) == \
+        _lib.PA_EINVAL
+    pool.v = 256
     pool.head_dim = 96
     assert lib.pa_cache_append(ctypes.byref(pool), 0, 256, 256, 256, 4, None) == _lib.PA_ENOTSUP
     del args
