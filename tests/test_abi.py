@@ -141,7 +141,8 @@ int main(void) {
   if (pa_bm_block_table(bm, 3, table, 4, &n) != PA_OK) return 4;
   printf("%d %d %d %d %d %d | %d | %d %d %d\n", slots[0], slots[1], slots[2], slots[3], slots[4], slots[5], ncow,
          n, table[0], table[1]);
-  printf("%d %s\n", pa_bm_append_slots(bm, 3, 100, slots, pairs, &ncow), pa_status_string(PA_ENOMEM));
+  int rc = pa_bm_append_slots(bm, 3, 100, slots, pairs, &ncow);
+  printf("%d %s\n", rc, pa_status_string(rc));
   pa_bm_destroy(bm);
   return 0;
 }
@@ -167,4 +168,4 @@ def test_header_is_c_and_the_library_links_from_c(tmp_path):
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines()
     # blocks come off the free order 7, 6, ...: slots 28..31 then 24, 25
     assert out[0] == "28 29 30 31 24 25 | 0 | 2 7 6"
-    assert out[1].split(" ", 1) == [str(_lib.PA_ENOMEM), "out of free blocks"]
+    assert out[1].startswith(f"{_lib.PA_ENOMEM} out of free blocks")
