@@ -141,3 +141,24 @@ def test_prefill_short_chunk_after_long_context_split(H_q, T, ctx_before):
     err = max_abs_err(out, ref)
     say("  max abs err", err)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("H_q,H_kv,T", [(32, 8, 8192), (8, 8, 4096)])
+def test_prefill_long_prompt_more_tiles_than_cus(H_q, H_kv, T):
+    """A whole long prompt in one chunk (no cached context): 1,024 and 128
+    workgroup tiles of 256 rows, several rounds over the 256 CUs.  Sampled
+    rows, including the first and last of tiles and of the chunk."""
+    rng = np.random.default_rng(T + H_q)
+    d, bs = 128, 16
+    say("prefill long prompt", H_q, H_kv, T)
+    op, gp, table = _chunk_world(rng, T, H_kv, d, bs, "bf16")
+    q32 = rng.standard_normal((T, H_q, d)).astype(np.float32)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    out = f64(_run(gp, q32, table, 0, scale, "bf16"))
+    tp = 256 // (H_q // H_kv)  # positions per workgroup tile
+    rows = sorted({0, 1, tp - 1, tp, 2 * tp + 5, T // 2, T - tp - 1, T - tp, T - 2, T - 1})
+    ref = attention.prefill_chunk(op, 0, widen(q32, "bf16"), table, 0, scale, rows=rows)
+    assert np.all(np.isfinite(out))
+    err = max_abs_err(out, ref, rows)
+    say("  max abs err", err)
+    assert err <= TOL["bf16"]
