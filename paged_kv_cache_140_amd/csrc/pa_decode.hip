@@ -44,8 +44,8 @@ __global__ void __launch_bounds__(MAXT)
     decode_kernel(char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off, int64_t head_stride,
                   const char* __restrict__ q, void* __restrict__ out, const int32_t* __restrict__ block_tables,
                   int32_t max_blocks, const int32_t* __restrict__ context_lens, float scale_log2, int32_t H_q,
-                  int32_t blocks_per_part, int32_t num_parts, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-                  const char* __restrict__ k_new, const char* __restrict__ v_new,
+                  int32_t blocks_per_part, int32_t num_parts, int32_t waves, float* __restrict__ ws_ml,
+                  float* __restrict__ ws_acc, const char* __restrict__ k_new, const char* __restrict__ v_new,
                   const int32_t* __restrict__ new_slots) {
   extern __shared__ float smem[];
   // Grid (kv head, partition slot, sequence), kv head fastest: workgroup i
@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(MAXT)
     part += blockIdx.z & 3;
     if (part >= num_parts) part -= num_parts;
   }
-  decode_body<E, D, G, BS, FUSED>(blockIdx.x, part, gridDim.x, blockIdx.z, smem, pool_k, pool_v, layer_off,
+  decode_body<E, D, G, BS, FUSED>(waves, blockIdx.x, part, gridDim.x, blockIdx.z, smem, pool_k, pool_v, layer_off,
                                   head_stride, q, out, block_tables, max_blocks, context_lens, scale_log2, H_q,
                                   blocks_per_part, num_parts, ws_ml, ws_acc, k_new, v_new, new_slots);
 }
@@ -214,7 +214,7 @@ static void launch_decode(const pa_kv_pool* pool, int32_t layer, void* out, cons
   hipLaunchKernelGGL((decode_kernel<E, D, G, BS, max_threads<G>(), FUSED>), grid, dim3(64 * pl.waves), lds, stream,
                      static_cast<char*>(pool->k), static_cast<char*>(pool->v), layer_off, head_stride,
                      static_cast<const char*>(q), out, bt, max_blocks, ctx, scale_log2, H_q, pl.blocks_per_part,
-                     pl.num_parts, ws.ml, ws.acc, static_cast<const char*>(nt.k), static_cast<const char*>(nt.v),
+                     pl.num_parts, pl.waves, ws.ml, ws.acc, static_cast<const char*>(nt.k), static_cast<const char*>(nt.v),
                      nt.slots);
   if (pl.num_parts > 1) launch_decode_merge(pool->dtype, D, out, ws, ctx, B, H_q, pl, BS, stream);
 }

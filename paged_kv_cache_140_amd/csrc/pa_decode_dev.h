@@ -167,10 +167,14 @@ __device__ __forceinline__ void gather_heads(const uint32_t* own, uint32_t* all)
 }
 
 // One workgroup's share of a decode: KV head g of sequence b, partition
-// ``part`` (blocks [part, part + 1) * blocks_per_part), H_kv KV heads.  smem
-// holds W * G * (D + 2) floats (W = waves of the workgroup).
+// ``part`` (blocks [part, part + 1) * blocks_per_part), H_kv KV heads.  W is
+// the workgroup's wave count, passed in rather than read from the dispatch:
+// the table entry of a wave's second unit depends on it, and a load of the
+// workgroup size would put one more memory round trip (which the scalar
+// wait counter cannot separate from the table loads) before the first K/V
+// loads.  smem holds W * G * (D + 2) floats.
 template <typename E, int D, int G, int BS, bool FUSED>
-__device__ __forceinline__ void decode_body(int g, int part, int H_kv, int b, float* __restrict__ smem,
+__device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, int b, float* __restrict__ smem,
                                             char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off,
                                             int64_t head_stride, const char* __restrict__ q, void* __restrict__ out,
                                             const int32_t* __restrict__ block_tables, int32_t max_blocks,
@@ -181,7 +185,6 @@ __device__ __forceinline__ void decode_body(int g, int part, int H_kv, int b, fl
   using Sh = DecodeShape<E, D, BS, G>;
   constexpr int S = Sh::S, VEC = Sh::VEC, LPT = Sh::LPT, TPW = Sh::TPW, NLD = Sh::NLD, U = Sh::U, UPB = Sh::UPB,
                 RING = Sh::RING;
-  const int W = blockDim.x >> 6;
   // Wave-uniform by construction; readfirstlane lets the compiler keep the
   // unit walk and the block-table reads in scalar registers / scalar loads,
   // so that a table read never waits on the vector loads in flight.
@@ -209,6 +212,9 @@ __device__ __forceinline__ void decode_body(int g, int part, int H_kv, int b, fl
   // Table entries of this wave's first RING units, read in parallel with the
   // sequence length instead of after it (the index is clamped to the row; an
   // entry past the sequence's end is simply not used).
+  // Fused: the new token's slot, read with the length and the table entries
+  // (one memory round trip for all of them, before the first K/V loads).
+  const int new_slot = FUSED ? __builtin_amdgcn_readfirstlane(new_slots[b]) : -1;
   int32_t ph[RING];
 #pragma unroll
   for (int p = 0; p < RING; ++p)
@@ -222,7 +228,7 @@ __device__ __forceinline__ void decode_body(int g, int part, int H_kv, int b, fl
     // an empty sequence: its rows are zeros.  Split partitions past the end
     // are not counted by the merge.
     if (num_parts == 1) {
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x) store_elem(E{}, out, head0 * D + i, 0.0f);
+      for (int i = threadIdx.x; i < G * D; i += W * 64) store_elem(E{}, out, head0 * D + i, 0.0f);
     }
     return;
   }
@@ -240,11 +246,9 @@ __device__ __forceinline__ void decode_body(int g, int part, int H_kv, int b, fl
   int vis = ctx;
   bool holds_new = false;
   bool owns_new = false;
-  int new_slot = -1;
   uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
   if constexpr (FUSED) {
     holds_new = (ctx - 1) / BS >= j0 && (ctx - 1) / BS < j1;
-    new_slot = __builtin_amdgcn_readfirstlane(new_slots[b]);
     owns_new = holds_new && new_slot >= 0;
     const int64_t new_row = (static_cast<int64_t>(b) * H_kv + g) * D * S;  // [B][H_kv][D] inputs
     kx = load16(k_new + new_row + c * 16);  // every lane: a fixed number of loads keeps the waits exact
@@ -590,7 +594,7 @@ __device__ __forceinline__ void decode_body(int g, int part, int H_kv, int b, fl
   }
   __syncthreads();
 
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+  for (int i = threadIdx.x; i < G * D; i += W * 64) {
     const int h = i / D;
     const int e = i % D;
     float mx = kNegInf;

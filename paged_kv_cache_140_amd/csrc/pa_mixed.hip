@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
     part += b & 3;
     if (part >= num_parts) part -= num_parts;
   }
-  decode_body<E, D, G, BS, false>(g, part, H_kv, b, reinterpret_cast<float*>(&lds[0][0]),
+  decode_body<E, D, G, BS, false>(kPrefillWaves, g, part, H_kv, b, reinterpret_cast<float*>(&lds[0][0]),
                                   pool_k, pool_v, layer_off, head_stride, dq, dout, block_tables, max_blocks,
                                   context_lens, scale_log2, H_q, blocks_per_part, num_parts, ws_ml, ws_acc, nullptr,
                                   nullptr, nullptr);
