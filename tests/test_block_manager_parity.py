@@ -6,7 +6,6 @@ import numpy as np
 import pytest
 
 from oracle.block_manager import BlockManager as OracleBM, OutOfBlocks as OracleOOB
-from oracle.run import OracleRun
 from pa_inputs import build_scenario, gen
 from paged_kv_cache_140_amd import BlockManager as LibBM, OutOfBlocks as LibOOB, PAError
 

@@ -1,7 +1,5 @@
 """pa_decode against the oracle on the five workloads and on edge cases."""
 
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -11,7 +9,7 @@ from oracle import attention, encoding
 from oracle.block_manager import BlockManager as OracleBM
 from oracle.pool import Pool
 from oracle.run import OracleRun, widen
-from pa_inputs import build_scenario, gen
+from pa_inputs import build_scenario
 
 pytestmark = pytest.mark.gpu
 

@@ -8,7 +8,6 @@ import pytest
 
 from oracle.block_manager import BlockManager, OutOfBlocks
 from oracle.pool import Pool
-from oracle import attention
 
 
 def identity_order(n):
