@@ -69,8 +69,8 @@ __global__ void __launch_bounds__(kPrefillThreads)
 // Combines the key splits of each chunk row (position, query head):
 // out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s, over
 // the splits that hold some of the keys of the row's position tile.  The
-// splits' weights are computed once, in LDS; each thread then sums its
-// dimension over the splits with four loads in flight.
+// splits' weights are computed once, in LDS; each thread sums its dimension
+// over the splits, the first 16 of them loaded before anything waits.
 template <typename E, int D>
 __global__ void __launch_bounds__(D)
     prefill_merge_kernel(void* __restrict__ out, const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
@@ -85,27 +85,56 @@ __global__ void __launch_bounds__(D)
   const int tile_steps = (ctx_before + t_last + 1 + kKeysPerStep - 1) / kKeysPerStep;
   const int ns = min(num_splits, (tile_steps + steps_per_split - 1) / steps_per_split);
   const int64_t stride = static_cast<int64_t>(T) * H_q;
+  // Every load is issued before any result is used: the first splits'
+  // outputs (one per thread and split) and, in wave 0, the splits' (m, l),
+  // so that the merge waits for one memory round trip, not three.
+  constexpr int kPre = 16;
+  const float* o = ws_o + row * D + e;
+  const int64_t so = stride * D;
+  float pre[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) pre[i] = i < ns ? o[i * so] : 0.0f;
   if (e < 64) {
-    // wave 0: the splits' (m, l), one split per lane, reduced by shuffles
-    float mx = -INFINITY;
-    for (int sp = e; sp < ns; sp += 64) mx = fmaxf(mx, ws_ml[2 * (sp * stride + row)]);
+    // wave 0: the splits' (m, l), one split per lane (64 at a time), reduced by shuffles
+    float2 ml[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int sp = e + 64 * r;
+      ml[r] = sp < ns ? *reinterpret_cast<const float2*>(ws_ml + 2 * (sp * stride + row)) : make_float2(-INFINITY, 0.0f);
+    }
+    float mx = fmaxf(ml[0].x, ml[1].x);
+    for (int sp = e + 128; sp < ns; sp += 64) mx = fmaxf(mx, ws_ml[2 * (sp * stride + row)]);
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     const float ms = mx == -INFINITY ? 0.0f : mx;
     float lt = 0.0f;
-    for (int sp = e; sp < ns; sp += 64) {
-      const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * (sp * stride + row));
-      const float w = __builtin_amdgcn_exp2f(ml.x - ms);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int sp = e + 64 * r;
+      if (sp < ns) {
+        const float w = __builtin_amdgcn_exp2f(ml[r].x - ms);
+        wt[sp] = w;
+        lt += ml[r].y * w;
+      }
+    }
+    for (int sp = e + 128; sp < ns; sp += 64) {
+      const float2 m2 = *reinterpret_cast<const float2*>(ws_ml + 2 * (sp * stride + row));
+      const float w = __builtin_amdgcn_exp2f(m2.x - ms);
       wt[sp] = w;
-      lt += ml.y * w;
+      lt += m2.y * w;
     }
     for (int off = 32; off > 0; off >>= 1) lt += __shfl_xor(lt, off);
     if (e == 0) wt[num_splits] = lt;
   }
   __syncthreads();
-  const float* o = ws_o + row * D + e;
-  const int64_t so = stride * D;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  int sp = 0;
+#pragma unroll
+  for (int i = 0; i < kPre; i += 4) {
+    if (i < ns) a0 += pre[i] * wt[i];
+    if (i + 1 < ns) a1 += pre[i + 1] * wt[i + 1];
+    if (i + 2 < ns) a2 += pre[i + 2] * wt[i + 2];
+    if (i + 3 < ns) a3 += pre[i + 3] * wt[i + 3];
+  }
+  int sp = kPre;
   for (; sp + 3 < ns; sp += 4) {
     a0 += o[(sp + 0) * so] * wt[sp + 0];
     a1 += o[(sp + 1) * so] * wt[sp + 1];
