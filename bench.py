@@ -101,9 +101,9 @@ def write_traffic_record(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
         "workload": "B=32, GQA 16/8, head_dim 128, block 16, ctx U[512,640]+1, seed 0, 28 layers rotated; one new "
                     "token per sequence appended in the same launch",
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -- python bench.py --no-cpu-baseline --no-rows",
-            "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -- python bench.py --no-cpu-baseline --no-rows",
-            "python bench.py --traffic-record gpurun_out/prof_fetch gpurun_out/prof_write",
+            f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -- python bench.py --no-cpu-baseline --no-rows",
+            f"rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -- python bench.py --no-cpu-baseline --no-rows",
+            f"python bench.py --traffic-record {fetch_dir} {write_dir}",
         ],
         "dispatches": n,
         "fetch_size_kib_per_dispatch_median": f_head,
@@ -210,7 +210,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         return 2
     import paged_kv_cache_140_amd as pa  # raises if libpa.so is missing
-    from paged_kv_cache_140_amd.runner import GpuRun
+    from paged_kv_cache_140_amd.runner import DeviceRun
     from pa_inputs import build_scenario
 
     pa.lib()
@@ -230,7 +230,7 @@ def main():
     scn = build_scenario(2, 0)
     cfg = scn.cfg
     L = args.layers
-    gpu = GpuRun(scn, device=dev, num_layers=L, fill="randn")
+    gpu = DeviceRun(scn, device=dev, num_layers=L, fill="randn")
     gpu.run_setup()
     step = scn.steps[0]
     si = gpu.prepare(step)
@@ -309,7 +309,7 @@ def main():
 
     # ---------------------------------------------------------- B=64: config 3
     scn3 = build_scenario(3, 0, bs=16)
-    g3 = GpuRun(scn3, device=dev, num_layers=1, fill="randn")
+    g3 = DeviceRun(scn3, device=dev, num_layers=1, fill="randn")
     g3.run_setup()
     si3 = g3.prepare(scn3.steps[0], longest_first=True)
     # the same step launched in batch order: the launch rows permuted back
@@ -338,7 +338,7 @@ def main():
     if not args.no_rows:
         rows = {}
         scn4 = build_scenario(4, 0)
-        g4 = GpuRun(scn4, device=dev, fill="randn")
+        g4 = DeviceRun(scn4, device=dev, fill="randn")
         g4.run_setup()
         tail = g4.prepare(scn4.steps[0])
         dec = g4.prepare(scn4.steps[1])
@@ -363,7 +363,7 @@ def main():
         torch.cuda.empty_cache()
 
         scn5 = build_scenario(5, 0)
-        g5 = GpuRun(scn5, device=dev, fill="randn")
+        g5 = DeviceRun(scn5, device=dev, fill="randn")
         g5.run_setup()
         s5 = g5.prepare(scn5.steps[0], longest_first=True)
         ms_d5 = time_loop(torch, lambda i: g5.launch(s5, do_copy=False, do_append=False, do_prefill=False), 10, 2)

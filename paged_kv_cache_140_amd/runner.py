@@ -44,7 +44,7 @@ class StepInputs:
     order: object = None
 
 
-class GpuRun:
+class DeviceRun:
     """``fill``: "nan" poisons every pool slot before setup (parity runs),
     "randn" fills it with N(0,1) on the device and skips writing the history
     values (timing runs only need the bookkeeping), None leaves it as is."""
