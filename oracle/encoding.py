@@ -48,7 +48,8 @@ def encode(x, dtype):
     if dtype == "bf16":
         return f32_to_bf16_bits(x)
     if dtype == "f16":
-        return x.astype(np.float16).view(np.uint16)
+        with np.errstate(over="ignore"):  # past the largest half, round-to-nearest gives infinity
+            return x.astype(np.float16).view(np.uint16)
     raise ValueError(dtype)
 
 

@@ -185,6 +185,7 @@ PLANTED = [
 
 
 @pytest.mark.parametrize("case", PLANTED, ids=[c[0] for c in PLANTED])
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")  # a planted mistake may overflow on purpose
 def test_planted_mistake_fails_a_pin(case, monkeypatch):
     _, module, old, new, pins = case
     plant(monkeypatch, module, old, new)
