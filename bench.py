@@ -333,6 +333,22 @@ def main():
                   "batch_order_ms_per_step": round(ms3_batch, 5)}
     del g3, si3, si3b
     torch.cuda.empty_cache()
+    # the same workload at the other block sizes it is specified over
+    sweep = {"16": {"ms_per_step": round(ms3, 5), "decode_ms": round(ms3d, 5),
+                    "decode_GBps": round(b3 / (ms3d * 1e-3) / 1e9, 1)}}
+    for bs in (8, 32):
+        scn_bs = build_scenario(3, 0, bs=bs)
+        g_bs = DeviceRun(scn_bs, device=dev, num_layers=1, fill="randn")
+        g_bs.run_setup()
+        si_bs = g_bs.prepare(scn_bs.steps[0], longest_first=True)
+        ms_f = time_loop(torch, lambda i: g_bs.launch(si_bs, fused=True), n3, 5)
+        ms_d = time_loop(torch, lambda i: g_bs.launch(si_bs, do_copy=False, do_append=False), n3, 5)
+        b_bs = decode_bytes(si_bs.lens.cpu().numpy(), 40, 40, 128, bs, 2)
+        sweep[str(bs)] = {"ms_per_step": round(ms_f, 5), "decode_ms": round(ms_d, 5),
+                          "decode_GBps": round(b_bs / (ms_d * 1e-3) / 1e9, 1)}
+        del g_bs, si_bs
+        torch.cuda.empty_cache()
+    out["b64"]["block_size_sweep"] = {k: sweep[k] for k in ("8", "16", "32")}
 
     # ---------------------------------------------------------- other rows
     if not args.no_rows:
