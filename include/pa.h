@@ -98,7 +98,8 @@ int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t n, hipS
 
 /*
  * Workspace bytes ``pa_decode`` needs for a batch (0 when it will not split a
- * sequence over several workgroups).  Depends on host-side sizes only.
+ * sequence over several workgroups).  Depends on host-side sizes, the
+ * current device's CU count and the tuning overrides only.
  */
 size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t B, int32_t H_q, int32_t max_ctx);
 
@@ -206,7 +207,7 @@ int pa_prefill_chunk(const pa_kv_pool* pool, int32_t layer, void* out, const voi
  *        More than the number of items is clamped to it.
  *   workspace: as pa_decode, for the decode half (pa_decode_workspace_size).
  *   bf16 and f16 pools only.  The decode half runs 8 waves per workgroup
- *   whatever PA_DECODE_WAVES says.  A split decode adds a second, small
+ *   whatever PA_TUNE_DECODE_WAVES says.  A split decode adds a second, small
  *   launch (the partition merge), as in pa_decode.
  */
 typedef struct pa_chunk {
@@ -232,6 +233,24 @@ int pa_mixed_batch(const pa_kv_pool* pool, int32_t layer, void* dec_out, const v
  * use under graph capture.  Returns the previous setting.
  */
 int pa_set_validate(int on);
+
+/*
+ * Tuning overrides of the grid plans, for sweeps and tests (0 = the
+ * library's own choice, the default).  Initial values come from the
+ * environment variables of the same names (PA_DECODE_WAVES,
+ * PA_DECODE_PART_BLOCKS, PA_PREFILL_SPLITS), read once at first use.
+ *   PA_TUNE_DECODE_WAVES:       waves per decode workgroup (capped at 16, or
+ *                               8 with more than 2 query heads per KV head).
+ *   PA_TUNE_DECODE_PART_BLOCKS: blocks per decode partition (a sequence
+ *                               longer than that is split and merged).
+ *   PA_TUNE_PREFILL_SPLITS:     1 never splits a prefill chunk over its keys;
+ *                               n > 1 asks for n splits whenever the caller
+ *                               gives a workspace.
+ * Process-wide; workspace sizes follow the current values.  Returns the
+ * previous value, or PA_EINVAL for an unknown key or a negative value.
+ */
+enum { PA_TUNE_DECODE_WAVES = 0, PA_TUNE_DECODE_PART_BLOCKS = 1, PA_TUNE_PREFILL_SPLITS = 2 };
+int pa_set_tuning(int key, int value);
 
 /* Message for a status code (thread-local copy of the last error detail). */
 const char* pa_status_string(int status);

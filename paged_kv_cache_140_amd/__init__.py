@@ -17,9 +17,11 @@ from .api import (  # noqa: F401
     pa_decode_append,
     pa_decode_workspace_size,
     pa_mixed_batch,
+    pa_set_tuning,
     pa_set_validate,
     pa_sha256,
     pa_prefill_chunk,
     pa_prefill_workspace_size,
     prefill_workspace,
+    tuning,
 )

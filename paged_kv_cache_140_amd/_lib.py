@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 PA_OK, PA_EINVAL, PA_ENOTSUP, PA_ENOMEM, PA_EHIP, PA_ENOENT, PA_ESPACE = 0, -1, -2, -3, -4, -5, -6
+PA_TUNE_DECODE_WAVES, PA_TUNE_DECODE_PART_BLOCKS, PA_TUNE_PREFILL_SPLITS = 0, 1, 2
 
 # Every symbol pa.h declares, with (restype, argtypes).
 _i32 = ctypes.c_int32
@@ -52,6 +53,7 @@ SIGNATURES = {
                                       ctypes.POINTER(ChunkStruct), _i32, _p, _i32, ctypes.c_float, _i32, _p,
                                       ctypes.c_size_t, _p]),
     "pa_set_validate": (ctypes.c_int, [ctypes.c_int]),
+    "pa_set_tuning": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_bm_create": (ctypes.c_int, [_i32, _i32, _pi32, ctypes.POINTER(_p)]),
     "pa_bm_destroy": (None, [_p]),

@@ -204,6 +204,38 @@ def pa_set_validate(on):
     return bool(lib().pa_set_validate(1 if on else 0))
 
 
+TUNING_KEYS = {"decode_waves": _lib.PA_TUNE_DECODE_WAVES, "decode_part_blocks": _lib.PA_TUNE_DECODE_PART_BLOCKS,
+               "prefill_splits": _lib.PA_TUNE_PREFILL_SPLITS}
+
+
+def pa_set_tuning(key, value):
+    """Set a grid-plan override ("decode_waves", "decode_part_blocks",
+    "prefill_splits"; 0 = the library's choice); returns the previous value."""
+    st = lib().pa_set_tuning(TUNING_KEYS[key], int(value))
+    if st < 0:
+        check(st, "pa_set_tuning")
+    return st
+
+
+class tuning:
+    """Context manager: grid-plan overrides for the duration of a block,
+    e.g. ``with tuning(decode_waves=4, decode_part_blocks=3): ...``."""
+
+    def __init__(self, **values):
+        self.values = values
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.values.items():
+            self.saved[k] = pa_set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            pa_set_tuning(k, v)
+        return False
+
+
 def pa_sha256(data):
     """SHA-256 digest (32 bytes) of ``data``, computed by the library."""
     data = bytes(data)

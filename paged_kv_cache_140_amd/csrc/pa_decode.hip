@@ -120,12 +120,6 @@ __global__ void __launch_bounds__(D)
 
 // ------------------------------------------------------------------- host
 
-int env_int(const char* name, int dflt) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  return std::atoi(s);
-}
-
 template <int G>
 constexpr int max_threads() {
   return G <= 2 ? 1024 : 512;
@@ -133,12 +127,13 @@ constexpr int max_threads() {
 
 static int max_waves_for(int G) { return (G <= 2 ? 1024 : 512) / 64; }
 
-// Grid plan from host-side sizes only (context lengths stay on the device).
-// Tuning overrides PA_DECODE_WAVES / PA_DECODE_PART_BLOCKS are read on every
-// call so that one process can sweep them.
+// Grid plan from host-side sizes and the device's CU count only (context
+// lengths stay on the device).  The tuning overrides (pa_set_tuning) fix the
+// wave count and the partition length.
 DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx) {
-  const int env_waves = env_int("PA_DECODE_WAVES", 0);
-  const int env_pb = env_int("PA_DECODE_PART_BLOCKS", 0);
+  const int env_waves = tuning(PA_TUNE_DECODE_WAVES);
+  const int env_pb = tuning(PA_TUNE_DECODE_PART_BLOCKS);
+  const int cus = device_cus();
   DecodePlan p;
   const int64_t nblk = ceil_div(max_ctx > 0 ? max_ctx : 1, bs);
   const int64_t pairs = static_cast<int64_t>(B) * H_kv;
@@ -146,7 +141,7 @@ DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx) {
   p.waves = p.waves > max_waves_for(G) ? max_waves_for(G) : p.waves;
   if (env_pb > 0) {
     p.blocks_per_part = env_pb;
-  } else if (pairs >= 256 && nblk <= 256) {
+  } else if (pairs >= cus && nblk <= 256) {
     // Enough (sequence, kv head) pairs to fill the chip and contexts short
     // enough that one workgroup per pair finishes in a few tens of
     // microseconds: a split would only add merge latency.
@@ -154,7 +149,7 @@ DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx) {
   } else {
     // Long contexts or few pairs: cut each sequence into partitions of at
     // least 64 blocks, enough that the hardware can balance ~4 per CU.
-    const int64_t parts = ceil_div(4 * 256, pairs);
+    const int64_t parts = ceil_div(4 * static_cast<int64_t>(cus), pairs);
     int64_t pb = ceil_div(nblk, parts);
     if (pb < 64) pb = 64;
     p.blocks_per_part = static_cast<int>(pb);

@@ -21,8 +21,13 @@ int check_pool(const pa_kv_pool* pool, int32_t layer);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Integer environment variable (tuning overrides), or dflt.
-int env_int(const char* name, int dflt);
+// Tuning overrides of the grid plans (0 = the library's own choice): read
+// once from PA_DECODE_WAVES, PA_DECODE_PART_BLOCKS and PA_PREFILL_SPLITS at
+// first use, changed by pa_set_tuning.
+int tuning(int key);
+
+// Compute units of the current device (queried once per device).
+int device_cus();
 
 // ---------------------------------------------------------------- validate
 // Validate mode (pa_set_validate / PA_VALIDATE): host checks of the device

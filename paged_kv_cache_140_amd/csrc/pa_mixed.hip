@@ -163,14 +163,6 @@ static MixedFn mixed_d(int D, int G, int bs) {
   return nullptr;
 }
 
-static int num_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                              hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
 // 64-key steps of all the chunks' items.
 static double chunk_steps(const pa_kv_pool* pool, const ChunkList& ch, int G) {
   const int TP = kRowsPerWave * kPrefillWaves / G;
@@ -200,7 +192,7 @@ static int default_prefill_wgs(const pa_kv_pool* pool, int B, int max_ctx, const
   const int elem = pool->dtype == PA_F32 ? 4 : 2;
   const double decode_us = static_cast<double>(B) * pool->num_kv_heads * 0.5 * max_ctx * 2.0 * pool->head_dim * elem /
                            5.0e6;
-  const int cap = std::min(n_items, num_cus());
+  const int cap = std::min(n_items, device_cus());
   if (decode_us <= 0.0) return cap;
   int n = static_cast<int>(std::ceil(1.5 * prefill_cu_us / decode_us));
   n = static_cast<int>(ceil_div(std::max(n, 8), 8) * 8);

@@ -160,24 +160,16 @@ struct PrefillPlan {
   int steps_per_split;
 };
 
-static int prefill_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                              hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
 static PrefillPlan plan_prefill(const pa_kv_pool* pool, int32_t T, int32_t H_q, int32_t ctx_before) {
   PrefillPlan p{1, 1 << 30};
   const int G = H_q / pool->num_kv_heads;
   const int TP = kRowsPerWave * kPrefillWaves / G;
   const int64_t items = ceil_div(T, TP) * pool->num_kv_heads;
   const int64_t steps = ceil_div(static_cast<int64_t>(ctx_before) + T, kKeysPerStep);
-  const int cus = prefill_cus();
-  // PA_PREFILL_SPLITS (read on every call, for sweeps): 1 never splits,
-  // n > 1 asks for n splits whenever a split is possible.
-  const int env_n = env_int("PA_PREFILL_SPLITS", 0);
+  const int cus = device_cus();
+  // Tuning override (pa_set_tuning): 1 never splits, n > 1 asks for n
+  // splits whenever a split is possible.
+  const int env_n = tuning(PA_TUNE_PREFILL_SPLITS);
   if (env_n == 1 || steps < 4 || (env_n == 0 && items * 2 > cus)) return p;
   int64_t n = env_n > 1 ? std::min<int64_t>(env_n, steps) : std::min<int64_t>(ceil_div(cus, items), steps / 4);
   const int64_t sps = ceil_div(steps, n);

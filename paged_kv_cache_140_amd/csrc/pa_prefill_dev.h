@@ -88,18 +88,18 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
 // lane l's bytes land at lds + 16*l; lds must be wave-uniform.  Written as
-// inline assembly (M0 = the LDS byte address, the low half of the generic
-// address) rather than the compiler's builtin: with a builtin load into LDS
-// in flight, the compiler's wait-count pass cannot separate LDS reads from
-// it and waits for every outstanding LDS read (lgkmcnt(0)) before the first
-// MFMA of each unit, instead of only the one that unit needs.  The kernel
-// tracks these loads itself (wait_loads_to_lds before the barrier that
-// precedes their first reader); M0 is set in the statement and used by
-// nothing else in these kernels.
+// inline assembly rather than the compiler's builtin: with a builtin load
+// into LDS in flight, the compiler's wait-count pass cannot separate LDS
+// reads from it and waits for every outstanding LDS read (lgkmcnt(0)) before
+// the first MFMA of each unit, instead of only the one that unit needs.  The
+// kernel tracks these loads itself (wait_loads_to_lds before the barrier
+// that precedes their first reader).  M0 (the LDS byte address, the low half
+// of the generic address) is an operand of the statement, so the compiler
+// itself writes it and knows its value afterwards.
 __device__ __forceinline__ void load_to_lds(const char* src, char* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 #endif
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as a builtin

@@ -1,6 +1,10 @@
-// Status codes, the thread-local last-error text and pool validation.
+// Status codes, the thread-local last-error text, pool validation, the
+// tuning overrides and the device's CU count.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
+#include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "pa_host.h"
@@ -39,7 +43,52 @@ int check_pool(const pa_kv_pool* pool, int32_t layer) {
   return PA_OK;
 }
 
+// ---------------------------------------------------------------- tuning
+namespace {
+constexpr int kTuneKeys = 3;
+const char* const kTuneEnv[kTuneKeys] = {"PA_DECODE_WAVES", "PA_DECODE_PART_BLOCKS", "PA_PREFILL_SPLITS"};
+std::atomic<int> g_tune[kTuneKeys];
+std::once_flag g_tune_once;
+
+void tune_init() {
+  std::call_once(g_tune_once, [] {
+    for (int k = 0; k < kTuneKeys; ++k) {
+      const char* s = std::getenv(kTuneEnv[k]);
+      const int v = (s && *s) ? std::atoi(s) : 0;
+      g_tune[k].store(v > 0 ? v : 0, std::memory_order_relaxed);
+    }
+  });
+}
+}  // namespace
+
+int tuning(int key) {
+  tune_init();
+  return g_tune[key].load(std::memory_order_relaxed);
+}
+
+// ---------------------------------------------------------------- devices
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 }  // namespace pa
+
+extern "C" int pa_set_tuning(int key, int value) {
+  if (key < 0 || key >= pa::kTuneKeys || value < 0) return pa::fail(PA_EINVAL, "pa_set_tuning: bad key or value");
+  pa::tune_init();
+  return pa::g_tune[key].exchange(value, std::memory_order_relaxed);
+}
 
 extern "C" const char* pa_status_string(int status) {
   static thread_local std::string msg;

@@ -19,3 +19,21 @@ def golden():
 
     with open(os.path.join(ROOT, "tests", "golden", "page_examples.json")) as f:
         return json.load(f)
+
+
+@pytest.fixture
+def tune():
+    """Grid-plan overrides of the library (pa_set_tuning) for one test,
+    restored afterwards: ``tune(decode_waves=4, decode_part_blocks=3)``."""
+    from paged_kv_cache_140_amd import pa_set_tuning
+
+    saved = {}
+
+    def set_(**values):
+        for k, v in values.items():
+            prev = pa_set_tuning(k, v)
+            saved.setdefault(k, prev)
+
+    yield set_
+    for k, v in saved.items():
+        pa_set_tuning(k, v)

@@ -134,14 +134,13 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[4]}-hq{c[0]}-hkv{c[1]}-d{c[2]}-bs{c[3]}" for c in CASES])
 @pytest.mark.parametrize("plan", [None, (1, 1), (4, 3), (8, 1000000)])
-def test_fused_edge_shapes_and_splits(case, plan, monkeypatch):
+def test_fused_edge_shapes_and_splits(case, plan, tune):
     """New token at a block start, a block end, a unit boundary, the first
     position, and in split partitions; its pool row starts as NaN, so any
     read of the pool at that position instead of the input shows up."""
     H_q, H_kv, d, bs, dtype, lengths = case
     if plan is not None:
-        monkeypatch.setenv("PA_DECODE_WAVES", str(plan[0]))
-        monkeypatch.setenv("PA_DECODE_PART_BLOCKS", str(plan[1]))
+        tune(decode_waves=plan[0], decode_part_blocks=plan[1])
     rng = np.random.default_rng(sum(lengths) + 3 * d)
     say("decode_append edge", case, plan)
     bm, op, N, slots = _history(rng, lengths, H_kv, d, bs, dtype)

@@ -154,10 +154,10 @@ def test_mixed_batch_matches_oracle_and_separate_calls(case):
 
 
 @pytest.mark.parametrize("part_blocks", [1, 3, 64])
-def test_mixed_batch_split_decode(part_blocks, monkeypatch):
+def test_mixed_batch_split_decode(part_blocks, tune):
     """Decode partitions forced small, so the decode half writes partials and
     the merge kernel runs after the mixed launch."""
-    monkeypatch.setenv("PA_DECODE_PART_BLOCKS", str(part_blocks))
+    tune(decode_part_blocks=part_blocks)
     H_q, H_kv, d, bs, dtype = 64, 8, 128, 16, "bf16"
     dec_lengths = [1, 300, 2049, 5000]
     chunks = [(700, 200), (90, 31)]
