@@ -155,6 +155,25 @@ int pa_decode_append(const pa_kv_pool* pool, int32_t layer, void* out, const voi
                      float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  A split decode keeps its partials in
+ * a static device array of PA_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends; the call itself allocates
+ * nothing.  Same arguments and same results, bit for bit, as pa_decode with
+ * a workspace.
+ *   Returns PA_ESPACE, with nothing launched, when the batch's split needs
+ *   more than PA_NOALLOC_SCRATCH_BYTES (pa_decode_workspace_size tells).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (concurrent streams, or host threads) race and must be serialised
+ *   by the caller.  Nothing in the array needs to start at zero.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_decode_noalloc(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B, int32_t H_q,
+                      const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t max_ctx,
+                      float scale, hipStream_t stream);
+
+/*
  * Workspace bytes pa_prefill_chunk can use to split a chunk over its keys
  * (0 when it would not split).  Depends on host-side sizes and the current
  * device's CU count only.

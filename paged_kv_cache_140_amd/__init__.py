@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     pa_copy_blocks,
     pa_decode,
     pa_decode_append,
+    pa_decode_noalloc,
     pa_decode_workspace_size,
     pa_mixed_batch,
     pa_set_tuning,

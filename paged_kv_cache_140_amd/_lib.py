@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 PA_OK, PA_EINVAL, PA_ENOTSUP, PA_ENOMEM, PA_EHIP, PA_ENOENT, PA_ESPACE = 0, -1, -2, -3, -4, -5, -6
 PA_TUNE_DECODE_WAVES, PA_TUNE_DECODE_PART_BLOCKS, PA_TUNE_PREFILL_SPLITS = 0, 1, 2
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol pa.h declares, with (restype, argtypes).
 _i32 = ctypes.c_int32
@@ -46,6 +47,8 @@ SIGNATURES = {
                                  ctypes.c_size_t, _p]),
     "pa_decode_append": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32,
                                         ctypes.c_float, _p, ctypes.c_size_t, _p]),
+    "pa_decode_noalloc": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _p, _i32, ctypes.c_float,
+                                         _p]),
     "pa_prefill_workspace_size": (ctypes.c_size_t, [_PPOOL, _i32, _i32, _i32]),
     "pa_prefill_chunk": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _i32, ctypes.c_float, _p,
                                         ctypes.c_size_t, _p]),

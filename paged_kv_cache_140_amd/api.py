@@ -109,6 +109,22 @@ def pa_decode(pool, layer, out, q, block_tables, context_lens, max_ctx, scale, w
                           _ptr(workspace), ws_bytes, _stream(stream)), "pa_decode")
 
 
+def pa_decode_noalloc(pool, layer, out, q, block_tables, context_lens, max_ctx, scale, stream=None):
+    """pa_decode with no workspace: a split keeps its partials in the
+    library's static per-GPU scratch (calls on one GPU must not overlap)."""
+    B, H_q, d = (int(x) for x in q.shape)
+    _need(q, "q", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(out, "out", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B][max_blocks]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    s = pool.struct()
+    check(lib().pa_decode_noalloc(ctypes.byref(s), layer, _ptr(out), _ptr(q), B, H_q, _ptr(block_tables),
+                                  int(block_tables.shape[1]), _ptr(context_lens), int(max_ctx), float(scale),
+                                  _stream(stream)), "pa_decode_noalloc")
+
+
 def pa_decode_append(pool, layer, out, q, k_new, v_new, slot_mapping, block_tables, context_lens, max_ctx, scale,
                      workspace=None, stream=None):
     """One decode step in one launch: append each sequence's new token

@@ -33,6 +33,7 @@
 
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "pa_decode_dev.h"
@@ -339,4 +340,59 @@ extern "C" int pa_decode_append(const pa_kv_pool* pool, int32_t layer, void* out
   return pa::decode_entry("pa_decode_append", pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens,
                           max_ctx, scale, workspace, workspace_bytes, pa::NewTokens{k_new, v_new, slot_mapping},
                           stream);
+}
+
+// ------------------------------------------------------ allocation-free decode
+// pa_decode_noalloc keeps a split decode's partials in this file-scope array
+// instead of a caller's workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in): the device address is
+// looked up once per device, with that device current, and kept.
+static __device__ __align__(256) float scratch[PA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace pa {
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_EHIP, std::string("pa_decode_noalloc: hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchDevices) return fail(PA_EINVAL, "pa_decode_noalloc: device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PA_EHIP, std::string("pa_decode_noalloc: hipGetSymbolAddress: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_decode_noalloc(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B,
+                                 int32_t H_q, const int32_t* block_tables, int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t max_ctx, float scale, hipStream_t stream) {
+  using namespace pa;
+  const char* who = "pa_decode_noalloc";
+  if (int e = validate_decode(who, pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens, max_ctx))
+    return e;
+  if (B == 0) return PA_OK;
+  const int G = H_q / pool->num_kv_heads;
+  const DecodePlan pl = plan_decode(B, pool->num_kv_heads, G, pool->block_size, max_ctx);
+  const size_t need = workspace_bytes_for(pl, B, pool->num_kv_heads, H_q, pool->head_dim);
+  if (need > PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ESPACE, std::string(who) + ": the split needs " + std::to_string(need) +
+                               " bytes of partials, more than the " + std::to_string(PA_NOALLOC_SCRATCH_BYTES) +
+                               "-byte static scratch; use pa_decode with a workspace");
+  void* ws = nullptr;
+  if (need > 0)
+    if (int e = scratch_address(&ws)) return e;
+  return decode_entry(who, pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens, max_ctx, scale, ws,
+                      need > 0 ? PA_NOALLOC_SCRATCH_BYTES : 0, NewTokens{nullptr, nullptr, nullptr}, stream);
 }
