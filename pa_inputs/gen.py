@@ -116,3 +116,50 @@ def churn(cfg, seed, add, try_append, free):
     for i in r.permutation(len(live)):
         free(live[int(i)])
     return next_id - 1_000_000
+
+
+# ---------------------------------------------------------------- signal inputs
+# N(0,1) queries and keys at scale 1/sqrt(d) spread a long context's softmax
+# almost evenly, so one 16-token group of 16k keys weighs ~1/1000 and moves
+# the output by ~1e-3: far below a bf16 tolerance of 2e-2.  In signal mode
+# every V row also carries a marker of its 16-token group: +-c at dim
+# (t // 16 + 37 g) mod d for KV head g, the sign flipping each time the
+# groups wrap round the d dims (so that a dim's markers cancel instead of
+# piling up over a long context), with c proportional to the sequence's
+# length.  Every group then moves one output dim by ~16 c / n =
+# 16 / SIGNAL_TOKENS_PER_UNIT: leaving a group out, counting it twice or
+# taking another head's rows shows as a change of several times the
+# tolerance at any context length.  A new token (a decode step's own row, or
+# a prefill chunk's row, which its row sees last) carries a second marker
+# weighing a whole group (16 c), so losing it, or a causal mask one key off,
+# shows too.  Queries are scaled by
+# SIGNAL_Q_SCALE, which keeps the weight of the lightest group within a
+# small factor of the mean.  The values stay N(0,1) plus the marker.
+SIGNAL_Q_SCALE = 0.5
+SIGNAL_TOKENS_PER_UNIT = 50.0
+SIGNAL_GROUP = 16
+
+
+def signal_c(final_len):
+    """Marker size of a sequence that reaches ``final_len`` visible tokens."""
+    return max(1.0, float(final_len) / SIGNAL_TOKENS_PER_UNIT)
+
+
+def position_signal(cfg, positions, c, new_token=False):
+    """Markers of V rows at ``positions`` (float32 [n][H_kv][d]): +-c at dim
+    (t // 16 + 37 g) mod d of head g, sign (-1)^((t // 16) // d).  A new
+    token (a decode step's appended row, or a prefill chunk's own row, the
+    last key its row sees) also carries a marker of a whole group's weight,
+    +-16 c at dim (t + 53 g) mod d, sign (-1)^(t // d)."""
+    pos = np.asarray(positions, dtype=np.int64).reshape(-1)
+    H, d = cfg["H_kv"], cfg["d"]
+    out = np.zeros((pos.size, H, d), dtype=np.float32)
+    grp = pos // SIGNAL_GROUP
+    gval = (np.float32(c) * np.where((grp // d) % 2 == 0, 1, -1)).astype(np.float32)
+    tval = (np.float32(c * SIGNAL_GROUP) * np.where((pos // d) % 2 == 0, 1, -1)).astype(np.float32)
+    rows = np.arange(pos.size)
+    for g in range(H):
+        out[rows, g, (grp + 37 * g) % d] += gval
+        if new_token:
+            out[rows, g, (pos + 53 * g) % d] += tval
+    return out

@@ -54,16 +54,40 @@ class Scenario:
     setup: list = field(default_factory=list)
     steps: List[Step] = field(default_factory=list)
     ctx: Optional[np.ndarray] = None  # per decode sequence, before the first step
+    # signal mode: marker size per sequence whose history is drawn
+    signal_c: dict = field(default_factory=dict)
 
     def history(self, seq, n):
         """History K/V of ``seq``'s first n tokens (float32 [n][H_kv][d] each)."""
-        return gen.history_kv(self.cfg, self.seed, seq, n)
+        k, v = gen.history_kv(self.cfg, self.seed, seq, n)
+        if self.cfg.get("signal"):
+            v += gen.position_signal(self.cfg, np.arange(int(n)), self.signal_c[seq])
+        return k, v
 
 
-def _decode_batch(cfg, seed, seqs, step_index):
+def _signal_new_rows(cfg, v, positions, cs, new_token):
+    """Signal mode: add the markers of appended rows (positions and marker
+    sizes per row) to their V."""
+    if cfg.get("signal"):
+        for i, (p, c) in enumerate(zip(positions, cs)):
+            v[i:i + 1] += gen.position_signal(cfg, [p], c, new_token=new_token)
+
+
+def _queries(cfg, seed, step_index, n):
+    q = gen.queries(cfg, seed, step_index, n)
+    if cfg.get("signal"):
+        q *= np.float32(gen.SIGNAL_Q_SCALE)
+    return q
+
+
+def _decode_batch(cfg, seed, seqs, step_index, positions=None, cs=None):
+    """One new token per sequence at ``positions`` (its length before the
+    append), then decode; ``cs``: signal-mode marker sizes."""
     T = len(seqs)
     k, v = gen.new_kv(cfg, seed, step_index, T)
-    q = gen.queries(cfg, seed, step_index, T)
+    if cfg.get("signal"):
+        _signal_new_rows(cfg, v, positions, cs, new_token=True)
+    q = _queries(cfg, seed, step_index, T)
     return Step(appends=[(s, 1) for s in seqs], k_new=k, v_new=v, decode_seqs=list(seqs), q=q)
 
 
@@ -74,18 +98,22 @@ def build_scenario(cid, seed=0, **overrides):
     if kind == "decode":
         ctx = gen.lengths(cfg, seed)
         scn.ctx = ctx
+        cs = [gen.signal_c(int(n) + 1) for n in ctx]
         if cfg.get("churn_rounds"):
             scn.setup.append(("churn",))
         for s, n in enumerate(ctx):
             scn.setup.append(("add", s))
             scn.setup.append(("append", s, int(n)))
-        scn.steps.append(_decode_batch(cfg, seed, list(range(cfg["B"])), 0))
+            scn.signal_c[s] = cs[s]
+        scn.steps.append(_decode_batch(cfg, seed, list(range(cfg["B"])), 0, [int(n) for n in ctx], cs))
     elif kind == "fork":
         P, S = cfg["prompts"], cfg["samples"]
+        c = gen.signal_c(cfg["prefix"] + cfg["tail"] + cfg["steps"])
         for p in range(P):
             root = p * S
             scn.setup.append(("add", root))
             scn.setup.append(("append", root, cfg["prefix"]))
+            scn.signal_c[root] = c
             for s in range(1, S):
                 scn.setup.append(("fork", root, root + s))
         seqs = list(range(P * S))
@@ -93,27 +121,38 @@ def build_scenario(cid, seed=0, **overrides):
         # tail: every sample writes its own 32 tokens after the shared prefix
         T = len(seqs) * cfg["tail"]
         k, v = gen.new_kv(cfg, seed, 0, T)
+        tail_pos = [cfg["prefix"] + j for _ in seqs for j in range(cfg["tail"])]
+        _signal_new_rows(cfg, v, tail_pos, [c] * T, new_token=False)
         scn.steps.append(Step(appends=[(s, cfg["tail"]) for s in seqs], k_new=k, v_new=v,
                               decode_seqs=[], q=np.zeros((0, cfg["H_q"], cfg["d"]), np.float32)))
         for i in range(cfg["steps"]):
-            scn.steps.append(_decode_batch(cfg, seed, seqs, 1 + i))
+            pos = [cfg["prefix"] + cfg["tail"] + i] * len(seqs)
+            scn.steps.append(_decode_batch(cfg, seed, seqs, 1 + i, pos, [c] * len(seqs)))
     elif kind == "mixed":
         ctx = gen.lengths(cfg, seed)
         scn.ctx = ctx
         B = cfg["B"]
+        cs = [gen.signal_c(int(n) + 1) for n in ctx]
         for s, n in enumerate(ctx):
             scn.setup.append(("add", s))
             scn.setup.append(("append", s, int(n)))
+            scn.signal_c[s] = cs[s]
         pseq = B
+        c_chunk = gen.signal_c(cfg["ctx_before"] + cfg["chunk"])
         scn.setup.append(("add", pseq))
         scn.setup.append(("append", pseq, cfg["ctx_before"]))
-        st = _decode_batch(cfg, seed, list(range(B)), 0)
+        scn.signal_c[pseq] = c_chunk
+        st = _decode_batch(cfg, seed, list(range(B)), 0, [int(n) for n in ctx], cs)
         kc, vc = gen.chunk_kv(cfg, seed, cfg["chunk"])
+        _signal_new_rows(cfg, vc, [cfg["ctx_before"] + t for t in range(cfg["chunk"])], [c_chunk] * cfg["chunk"],
+                         new_token=True)
         st.appends.append((pseq, cfg["chunk"]))
         st.k_new = np.concatenate([st.k_new, kc])
         st.v_new = np.concatenate([st.v_new, vc])
-        st.prefill = Prefill(seq=pseq, ctx_before=cfg["ctx_before"], T=cfg["chunk"],
-                             q=gen.chunk_queries(cfg, seed, cfg["chunk"]))
+        qc = gen.chunk_queries(cfg, seed, cfg["chunk"])
+        if cfg.get("signal"):
+            qc *= np.float32(gen.SIGNAL_Q_SCALE)
+        st.prefill = Prefill(seq=pseq, ctx_before=cfg["ctx_before"], T=cfg["chunk"], q=qc)
         scn.steps.append(st)
     elif kind == "beam":
         # Every prompt starts ``beam`` beams sharing its blocks (its last one
@@ -123,10 +162,12 @@ def build_scenario(cid, seed=0, **overrides):
         # beam appends one token and is decoded.
         P, k = cfg["prompts"], cfg["beam"]
         beams, next_id = [], []
+        c = gen.signal_c(cfg["prompt_len"] + cfg["steps"])
         for p in range(P):
             root = p * 1000
             scn.setup.append(("add", root))
             scn.setup.append(("append", root, cfg["prompt_len"]))
+            scn.signal_c[root] = c
             for j in range(1, k):
                 scn.setup.append(("fork", root, root + j))
             beams.append([root + j for j in range(k)])
@@ -146,7 +187,8 @@ def build_scenario(cid, seed=0, **overrides):
                         next_id[p] += 1
                 ops += [("free", b) for b in beams[p] if b not in kept]
                 beams[p] = sorted(new)
-            st = _decode_batch(cfg, seed, sorted(b for bs_ in beams for b in bs_), t)
+            seqs = sorted(b for bs_ in beams for b in bs_)
+            st = _decode_batch(cfg, seed, seqs, t, [cfg["prompt_len"] + t] * len(seqs), [c] * len(seqs))
             st.ops = ops
             scn.steps.append(st)
         scn.ctx = np.full(P * k, cfg["prompt_len"], dtype=np.int64)

@@ -16,12 +16,22 @@ pytestmark = pytest.mark.gpu
 
 # ------------------------------------------------------------------ workloads
 
+# ``signal``: the inputs whose every block, new token and KV head moves the
+# checked rows by more than the tolerance (pa_inputs signal mode; shown by
+# tests/test_parity_inputs_catch_kernel_mistakes.py); plain N(0,1) otherwise.
 @pytest.mark.parametrize("cid,over,seed", [
     (1, {}, 0), (1, {}, 1), (1, {}, 2),
     (2, {}, 0), (2, {}, 1), (2, {}, 2),
+    (2, {"signal": True}, 0), (2, {"signal": True}, 1), (2, {"signal": True}, 2),
     (3, {"bs": 8}, 0), (3, {"bs": 16}, 0), (3, {"bs": 32}, 0),
+    (3, {"bs": 8, "signal": True}, 0), (3, {"bs": 16, "signal": True}, 0), (3, {"bs": 32, "signal": True}, 0),
+    (3, {"bs": 8, "signal": True}, 1), (3, {"bs": 16, "signal": True}, 1), (3, {"bs": 32, "signal": True}, 1),
+    (3, {"bs": 8, "signal": True}, 2), (3, {"bs": 16, "signal": True}, 2), (3, {"bs": 32, "signal": True}, 2),
 ])
 def test_decode_step_matches_oracle(cid, over, seed):
+    """One append + decode step of the workload: slots bit-exact, the pools
+    after the plain pa_cache_append bit-exact with the oracle's (every slot,
+    the NaN-poisoned ones included), every decode row within tolerance."""
     from paged_kv_cache_140_amd.runner import DeviceRun
 
     scn = build_scenario(cid, seed, **over)
@@ -37,31 +47,37 @@ def test_decode_step_matches_oracle(cid, over, seed):
         torch.cuda.synchronize()
         assert list(si.host_slots) == ores.slots
         assert si.lens.cpu().tolist() == ores.decode_lengths
+        assert np.array_equal(bits(gpu.pool.k), orc.pool.k) and np.array_equal(bits(gpu.pool.v), orc.pool.v)
         err = max_abs_err(f64(si.out), ores.decode_out)
         say("  max abs err", err, "tol", TOL[dt])
         assert err <= TOL[dt]
 
 
-def test_decode_shared_prefix_sampling_all_steps():
+@pytest.mark.parametrize("seed,signal,all_rows", [(0, False, False), (0, True, True), (1, True, False),
+                                                  (2, True, False)])
+def test_decode_shared_prefix_sampling_all_steps(seed, signal, all_rows):
     """Config 4 in full: prefix 3,000 x 8 prompts, 8 samples each (refcount 8),
-    56 copy-on-write copies, 16 append+decode steps."""
+    56 copy-on-write copies, 16 append+decode steps.  Every row of every step
+    (``all_rows``), or every row of the first and last steps and four rows of
+    the others."""
     from paged_kv_cache_140_amd.runner import DeviceRun
 
-    scn = build_scenario(4, 0)
-    say("decode workload 4")
+    scn = build_scenario(4, seed, signal=signal)
+    say("decode workload 4 seed", seed, "signal" if signal else "")
     orc = OracleRun(scn)
     orc.run_setup()
     gpu = DeviceRun(scn)
     gpu.run_setup()
     worst = 0.0
     for i, st in enumerate(scn.steps):
-        rows = None if i in (1, len(scn.steps) - 1) else [0, 7, 8, 63]
+        rows = None if all_rows or i in (1, len(scn.steps) - 1) else [0, 7, 8, 63]
         ores = orc.run_step(st, decode_rows=rows)
         si = gpu.run_step(st)
         torch.cuda.synchronize()
         assert [tuple(p) for p in si.host_pairs.tolist()] == ores.pairs
         if i == 0:
             assert len(ores.pairs) == 56
+        if i in (0, 1, len(scn.steps) - 1):
             assert np.array_equal(bits(gpu.pool.k), orc.pool.k) and np.array_equal(bits(gpu.pool.v), orc.pool.v)
         if st.decode_seqs:
             worst = max(worst, max_abs_err(f64(si.out), ores.decode_out, rows if rows else slice(None)))
@@ -69,34 +85,72 @@ def test_decode_shared_prefix_sampling_all_steps():
     assert worst <= TOL["bf16"]
 
 
-def test_decode_mixed_batch_full_size_sampled():
-    """Config 5 at full size (63 sequences of 1k-32k tokens): sampled
-    sequences against the oracle computed one by one on contiguous K/V."""
+def _contiguous_kv(scn, st, i, rows_new):
+    """Sequence i's K/V as the step's attention sees it: its history then
+    its appended rows (float64 [H_kv][n][d], the stored bf16 values)."""
+    k, v = scn.history(i, int(scn.ctx[i]) if i < len(scn.ctx) else st.prefill.ctx_before)
+    k = np.concatenate([widen(k, "bf16"), widen(st.k_new[rows_new], "bf16")]).transpose(1, 0, 2)
+    v = np.concatenate([widen(v, "bf16"), widen(st.v_new[rows_new], "bf16")]).transpose(1, 0, 2)
+    return k, v
+
+
+@pytest.mark.parametrize("seed,signal", [(0, True), (1, True), (2, True)])
+def test_decode_long_contexts_full_size_every_row(seed, signal):
+    """Config 5's decode at full size (63 sequences of 1k-32k tokens, 64/8
+    heads): after the step's plain appends (the 63 new tokens and the
+    1,024-row chunk), the written rows are bit-exact and nothing else in the
+    4.3 GB pools changed (poisoned slots included); then every decode row
+    against the oracle computed one by one on contiguous K/V."""
     from paged_kv_cache_140_amd.runner import DeviceRun
 
-    scn = build_scenario(5, 0)
+    scn = build_scenario(5, seed, signal=signal)
     cfg = scn.cfg
     st = scn.steps[0]
-    say("decode workload 5 setup")
+    say("decode workload 5 setup, seed", seed, "signal" if signal else "")
     gpu = DeviceRun(scn)
     gpu.run_setup()
     si = gpu.prepare(st)
-    gpu.launch(si, do_prefill=False)
+    before_k, before_v = gpu.pool.k.clone(), gpu.pool.v.clone()
+    gpu.launch(si, do_decode=False, do_prefill=False)
+    torch.cuda.synchronize()
+    _check_appended_rows(gpu.pool, before_k, before_v, si.host_slots, st, cfg)
+    del before_k, before_v
+    gpu.launch(si, do_copy=False, do_append=False, do_prefill=False)
     torch.cuda.synchronize()
     got = f64(si.out)
-    ctx = scn.ctx
-    rows = sorted({0, int(np.argmax(ctx)), int(np.argmin(ctx)), 31, 62})
+    assert np.all(np.isfinite(got))
     q = widen(st.q, "bf16")
     worst = 0.0
-    for i in rows:
-        k, v = scn.history(i, int(ctx[i]))
-        k = np.concatenate([widen(k, "bf16"), widen(st.k_new[i:i + 1], "bf16")]).transpose(1, 0, 2)
-        v = np.concatenate([widen(v, "bf16"), widen(st.v_new[i:i + 1], "bf16")]).transpose(1, 0, 2)
+    for i in range(len(st.decode_seqs)):
+        k, v = _contiguous_kv(scn, st, i, slice(i, i + 1))
         ref = attention.attend(q[i], k, v, cfg["scale"])
         worst = max(worst, float(np.max(np.abs(got[i] - ref))))
-    assert np.all(np.isfinite(got))
     say("  max abs err", worst)
     assert worst <= TOL["bf16"]
+
+
+def _check_appended_rows(pool, before_k, before_v, slots, st, cfg):
+    """Pool after a plain pa_cache_append of the step's rows: each written
+    slot holds exactly the oracle's bf16 encoding of its row; every other
+    element of the pool (the other slots of the written blocks, NaN-poisoned
+    or holding history, and every other block) is bit for bit what it was."""
+    bs = cfg["bs"]
+    sl = torch.from_numpy(np.asarray(slots, dtype=np.int64)).cuda()
+    blk, off = sl // bs, sl % bs
+    for t_pool, t_before, new in ((pool.k, before_k, st.k_new), (pool.v, before_v, st.v_new)):
+        got_rows = bits(t_pool[0][:, blk, off, :].transpose(0, 1))  # [T][H_kv][d]
+        assert np.array_equal(got_rows, encoding.encode(new, "bf16"))
+        t_before[0][:, blk, off, :] = t_pool[0][:, blk, off, :]
+        assert torch.equal(t_pool.view(torch.int16), t_before.view(torch.int16))
+    # the slots after each written row in its block are still the poison
+    last = {}
+    for s_ in slots:
+        last[int(s_) // bs] = max(last.get(int(s_) // bs, -1), int(s_) % bs)
+    blocks = torch.tensor(sorted(last), dtype=torch.int64).cuda()
+    poison = encoding.nan_bits("bf16")
+    kb = bits(pool.k[0][:, blocks])  # [H_kv][nblocks][bs][d]
+    for j, b in enumerate(sorted(last)):
+        assert np.all(kb[:, j, last[b] + 1:] == poison)
 
 
 # ------------------------------------------------------------------ edge cases

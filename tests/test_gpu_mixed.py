@@ -194,14 +194,17 @@ def test_mixed_batch_one_half_empty(which):
         assert max_abs_err(f64(mp), pref) <= TOL[dtype]
 
 
-def test_mixed_batch_full_size_sampled():
+@pytest.mark.parametrize("signal", [False, True])
+def test_mixed_batch_full_size_sampled(signal):
     """The mixed workload at full size -- 63 decodes of 1k-32k tokens and the
     1,024-token chunk after 3,500 cached tokens, 64 query / 8 KV heads -- as
-    one pa_mixed_batch: bit for bit equal to the separate calls, and sampled
-    rows of both halves against the oracle on contiguous K/V."""
+    one pa_mixed_batch: bit for bit equal to the separate calls (whose every
+    decode row the decode tests check on the same inputs), sampled decode
+    rows and the first and last position of every chunk position tile
+    against the oracle on contiguous K/V."""
     from paged_kv_cache_140_amd.runner import DeviceRun
 
-    scn = build_scenario(5, 0)
+    scn = build_scenario(5, 0, signal=signal)
     cfg, st = scn.cfg, scn.steps[0]
     say("mixed workload 5 setup")
     gpu = DeviceRun(scn)
@@ -231,7 +234,7 @@ def test_mixed_batch_full_size_sampled():
     k, v = scn.history(pf.seq, pf.ctx_before)
     kc = np.concatenate([widen(k, "bf16"), widen(st.k_new[-pf.T:], "bf16")]).transpose(1, 0, 2)
     vc = np.concatenate([widen(v, "bf16"), widen(st.v_new[-pf.T:], "bf16")]).transpose(1, 0, 2)
-    rows = [0, 255, 256, 1023]
+    rows = sorted({r for t0 in range(0, pf.T, 256 // cfg["G"]) for r in (t0, t0 + 256 // cfg["G"] - 1)})
     ref = attention.causal_rows(widen(pf.q, "bf16"), kc, vc, pf.ctx_before, cfg["scale"], rows)
     worst = max(worst, max_abs_err(got_p, ref, rows))
     say("  max abs err", worst)

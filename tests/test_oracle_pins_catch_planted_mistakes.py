@@ -102,6 +102,7 @@ PC = [T_PC.test_key_is_sha256_of_previous_key_tokens_and_extra,
       T_PC.test_only_full_blocks_page_prefix_workload, T_PC.test_freed_blocks_wait_tail_first_and_lru_is_evicted_first,
       T_PC.test_hits_on_live_blocks_share_them, T_PC.test_append_without_token_ids_stops_keying,
       T_PC.test_failed_append_changes_nothing, T_PC.test_identity_pool_fuzz]
+ADM = [T_PC.test_admission_queries_closed_forms, T_PC.test_admission_queries_equal_their_effect]
 CAP = [T_CAP.test_page_illustration, T_CAP.test_lognormal_lengths_waste_below_one_block,
        T_CAP.test_active_requests_in_the_page_pool, T_CAP.test_shared_blocks_count_once]
 RUN = [T_RUN.test_config1_paged_equals_logical_and_uses_12_blocks, T_RUN.test_config4_copy_on_write_pairs_small,
@@ -152,6 +153,16 @@ PLANTED = [
      "if len(part) == self.block_size or p == self.length[seq] + n - 1:", PC),
     ("no-eviction", "oracle.block_manager", "            del self.cache[self.key_of.pop(b)]\n", "            pass\n", PC),
     ("hit-not-pulled-from-queue", "oracle.block_manager", "                self.free.remove(b)\n", "                pass\n", PC),
+    # admission queries
+    ("blocks-needed-ignores-cow", "oracle.block_manager",
+     "cow = 1 if ln % bs and self.ref[tab[-1]] > 1 else 0", "cow = 0", ADM),
+    ("blocks-needed-cow-on-full-block", "oracle.block_manager",
+     "cow = 1 if ln % bs and self.ref[tab[-1]] > 1 else 0", "cow = 1 if tab and self.ref[tab[-1]] > 1 else 0", ADM),
+    ("blocks-needed-rounds-down", "oracle.block_manager",
+     "fresh = -(-(ln + n) // bs) - len(tab)", "fresh = (ln + n) // bs - len(tab)", ADM),
+    ("admit-cost-ignores-waiting-hits", "oracle.block_manager", "            waiting += self.ref[b] == 0\n", "", ADM),
+    ("admit-cost-ignores-hits", "oracle.block_manager",
+     "return waiting + -(-len(tokens) // bs) - hits", "return waiting + -(-len(tokens) // bs)", ADM),
     # capacity
     ("shared-blocks-counted-twice", "oracle.capacity", "blocks = set()", "blocks = []", CAP),
     ("waste-off-by-one", "oracle.capacity", "return [len(bm.block_table(s)) * bm.block_size - bm.seq_len(s) for s in seqs]",
@@ -194,4 +205,4 @@ def test_planted_mistake_fails_a_pin(case, monkeypatch):
 
 
 def test_pins_pass_on_the_oracle_as_it_is():
-    assert first_failure(ATT + ENC + PC[:4] + CAP + RUN[:1] + POOL) is None
+    assert first_failure(ATT + ENC + PC[:4] + ADM + CAP + RUN[:1] + POOL) is None

@@ -221,3 +221,94 @@ def test_identity_pool_fuzz(seed):
             except OutOfBlocks:
                 pass
         _check_identity(bm, pool, want)
+
+
+# ------------------------------------------------ admission queries (oracle only)
+# blocks_needed and admit_cost are what a scheduler compares with the free
+# block count before it admits, lets wait or preempts ([icarus] "改善调度与回收";
+# [ttlab] "5. KV 자리가 모자라면").  Their pin is their effect: the query must
+# equal the free blocks the operation then takes, and the operation must fail
+# exactly when the query exceeds the free count.
+
+def test_admission_queries_closed_forms():
+    """Hand-worked cases at block size 4: a fresh sequence, a partly filled
+    last block, a shared partly filled block (copy-on-write costs one more),
+    a shared full block (no copy), and a prompt whose cached prefix waits in
+    the free queue or is held by a live sequence."""
+    bm = BlockManager(16, 4, list(range(16)))
+    bm.add_seq(0)
+    assert bm.blocks_needed(0, 0) == 0
+    assert bm.blocks_needed(0, 1) == 1
+    assert bm.blocks_needed(0, 9) == 3          # ceil(9 / 4)
+    bm.append_slots(0, 6)                       # blocks 0, 1; block 1 half full
+    assert bm.blocks_needed(0, 2) == 0          # fits in block 1
+    assert bm.blocks_needed(0, 3) == 1
+    bm.fork(0, 1)                               # block 1 shared, half full
+    assert bm.blocks_needed(1, 1) == 1          # copy-on-write of block 1
+    assert bm.blocks_needed(1, 3) == 2          # the copy + one new block
+    bm.append_slots(0, 2)                       # seq 0 copies block 1, fills its copy
+    bm.add_seq(2)
+    bm.append_slots(2, 8)
+    bm.fork(2, 3)                               # seq 3 shares two full blocks
+    assert bm.blocks_needed(3, 1) == 1          # a new block, no copy
+    # prefix cache: keyed sequence 4 with 8 tokens = 2 full cached blocks
+    prompt = list(range(100, 108))
+    bm.add_seq_prefix(4, prompt)
+    bm.append_tokens(4, prompt)
+    free0 = bm.num_free()
+    assert bm.admit_cost(prompt + [1, 2, 3]) == 1          # both blocks live: only the tail block
+    assert bm.admit_cost([9] + prompt) == 3                # no hit: ceil(9 / 4)
+    bm.free_seq(4)                                         # its blocks wait in the free queue
+    assert bm.num_free() == free0 + 2
+    assert bm.admit_cost(prompt + [1, 2, 3]) == 3          # two waiting hits + the tail block
+    assert bm.admit_cost(prompt[:4]) == 1                  # one waiting hit, nothing else
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_admission_queries_equal_their_effect(seed):
+    """Random admits, forks, frees and appends with token ids: before each
+    admission or append, its query equals the drop in free blocks that
+    follows, and the operation runs out of blocks exactly when the query is
+    larger than the free count (then nothing changes)."""
+    rng = np.random.default_rng(500 + seed)
+    bs = int(rng.choice([1, 2, 4, 8]))
+    N = int(rng.integers(6, 40))
+    bm = BlockManager(N, bs, rng.permutation(N))
+    bases = [[int(x) for x in rng.integers(0, 5, 5 * bs)] for _ in range(3)]
+    live, nxt, checked = [], 0, 0
+    for _ in range(400):
+        x = rng.random()
+        if x < 0.3 or not live:
+            base = bases[int(rng.integers(3))]
+            prompt = base[:int(rng.integers(0, len(base) + 1))] + \
+                [int(t) for t in rng.integers(0, 5, int(rng.integers(0, 3 * bs)))]
+            cost, free = bm.admit_cost(prompt), bm.num_free()
+            hit = bm.add_seq_prefix(nxt, prompt)
+            try:
+                bm.append_tokens(nxt, prompt[hit:])
+                assert cost <= free and free - bm.num_free() == cost
+                live.append(nxt)
+            except OutOfBlocks:
+                assert cost > free
+                bm.free_seq(nxt)  # give back the hit blocks it took
+            checked += 1
+            nxt += 1
+        elif x < 0.4:
+            p = live[int(rng.integers(len(live)))]
+            bm.fork(p, nxt)
+            live.append(nxt)
+            nxt += 1
+        elif x < 0.55:
+            bm.free_seq(live.pop(int(rng.integers(len(live)))))
+        else:
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 2 * bs + 2))
+            need, free = bm.blocks_needed(s, n), bm.num_free()
+            before = bm.block_table(s)
+            try:
+                bm.append_tokens(s, [int(t) for t in rng.integers(0, 5, n)])
+                assert need <= free and free - bm.num_free() == need
+            except OutOfBlocks:
+                assert need > free and bm.block_table(s) == before and bm.num_free() == free
+            checked += 1
+    assert checked > 150

@@ -1,0 +1,219 @@
+"""The full-size GPU parity inputs can fail.
+
+A parity test only means something if a plausible kernel mistake would move
+the rows it checks by more than its tolerance (2e-2 max-abs for bf16).  With
+N(0,1) queries and keys at scale 1/sqrt(d), a long context spreads its
+softmax almost evenly, and one 16-token block of 16k keys moves the output by
+~1e-3.  The GPU parity tests therefore also run every workload on the
+signal-mode inputs of ``pa_inputs`` (markers in V, damped queries), and this
+CPU test shows, on the oracle's own float64 attention and the same seeded
+inputs, that on those inputs each of these mistakes moves the checked rows by
+more than the tolerance:
+
+  * leaving out any one block of the sequence (every block, so every split,
+    partition, unit and 64-key boundary the kernels might get wrong is
+    covered, whatever the split plan);
+  * counting any one block twice;
+  * leaving out the step's new token (decode) or the row's own key (the
+    chunk's causal diagonal), and letting a chunk row see the next key;
+  * reading the K/V of the wrong KV head.
+
+The effect of a block is computed exactly from the softmax weights: with
+P_b the weight of block b and W_b its weighted V sum, dropping it gives
+(out - W_b) / (1 - P_b) and duplicating it (out + W_b) / (1 + P_b).  The
+plain N(0,1) inputs are checked too, to record that they cannot catch a
+dropped block (the reason the signal inputs exist).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import attend
+from oracle.run import OracleRun
+from pa_inputs import build_scenario
+
+
+def widen(x, dtype):
+    """The stored 16-bit value of float32 input as float64.  torch's CPU
+    round-to-nearest-even (what oracle.encoding is pinned to, and ~10x
+    faster on the millions of history values here)."""
+    assert dtype == "bf16"
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(torch.float64).numpy()
+
+TOL_BF16 = 2e-2
+MISTAKES = ("drop_block", "dup_block", "drop_new", "wrong_head")
+
+
+def _weights(q, k, scale):
+    """Softmax weights of the G query heads of each KV head: [H_kv][G][n]."""
+    H_q, d = q.shape
+    H_kv = k.shape[0]
+    G = H_q // H_kv
+    s = scale * np.einsum("ghd,gnd->ghn", q.reshape(H_kv, G, d), k)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    return p / p.sum(axis=-1, keepdims=True)
+
+
+def mistake_effects(q, k, v, bs, scale):
+    """Smallest max-abs change of a KV head's G output rows, over every
+    block (drop / duplicate), the last key (drop), and over KV heads (read
+    head g+1's K/V instead of g's).  q [H_q][d], k, v [H_kv][n][d]."""
+    H_kv, n, d = k.shape
+    p = _weights(q, k, scale)  # [H_kv][G][n]
+    out = np.einsum("ghn,gnd->ghd", p, v)
+    nb = -(-n // bs)
+    pp = np.zeros(p.shape[:2] + (nb * bs,))
+    pp[..., :n] = p
+    vp = np.zeros((H_kv, nb * bs, d))
+    vp[:, :n] = v
+    pb = pp.reshape(H_kv, -1, nb, bs)
+    P = pb.sum(-1)[..., None]                                     # [H_kv][G][nb][1]
+    W = np.einsum("ghbt,gbtd->ghbd", pb, vp.reshape(H_kv, nb, bs, d))
+    o = out[:, :, None, :]
+    drop = np.abs((P * o - W) / (1.0 - P)).max(axis=(1, 3))      # [H_kv][nb]
+    dup = np.abs((W - P * o) / (1.0 + P)).max(axis=(1, 3))
+    pl = p[..., -1:]
+    drop_new = np.abs((pl * out - pl * v[:, None, -1, :]) / (1.0 - pl)).max(axis=(1, 2))
+    k2, v2 = np.roll(k, -1, axis=0), np.roll(v, -1, axis=0)
+    wrong = np.abs(np.einsum("ghn,gnd->ghd", _weights(q, k2, scale), v2) - out).max(axis=(1, 2))
+    # Counting the only block of a one-block sequence twice changes no
+    # softmax result: nothing to detect there.
+    return {"drop_block": drop.min(), "dup_block": dup.min() if nb > 1 else np.inf,
+            "drop_new": drop_new.min(), "wrong_head": wrong.min()}
+
+
+def _fold(worst, e):
+    for key, val in e.items():
+        worst[key] = min(worst.get(key, np.inf), float(val))
+    return worst
+
+
+def decode_inputs(cid, seed, rows=None, **over):
+    """(q, k, v) of the checked rows of the workload's last decode step, K/V
+    as the sequence sees them (float64, the stored bf16 values), from the
+    oracle's logical view."""
+    scn = build_scenario(cid, seed, **over)
+    cfg = scn.cfg
+    if len(scn.steps) == 1 and scn.ctx is not None and cfg["kind"] in ("decode", "mixed"):
+        st = scn.steps[0]
+        q = widen(st.q, cfg["dtype"])
+        for i in (range(len(st.decode_seqs)) if rows is None else rows):
+            k, v = scn.history(i, int(scn.ctx[i]))
+            k = np.concatenate([widen(k, cfg["dtype"]), widen(st.k_new[i:i + 1], cfg["dtype"])]).transpose(1, 0, 2)
+            v = np.concatenate([widen(v, cfg["dtype"]), widen(st.v_new[i:i + 1], cfg["dtype"])]).transpose(1, 0, 2)
+            yield cfg, q[i], k, v
+        return
+    orc = OracleRun(scn, with_pool=False)
+    orc.run_setup()
+    for st in scn.steps:
+        orc.run_step(st, paged=False, decode_rows=[])
+    st = scn.steps[-1]
+    q = widen(st.q, cfg["dtype"])
+    for i in (range(len(st.decode_seqs)) if rows is None else rows):
+        k, v = orc.logical_kv(st.decode_seqs[i])
+        yield cfg, q[i], k, v
+
+
+def _decode_worst(cid, seed, rows=None, block_sizes=None, **over):
+    """Worst effect of each mistake over the checked rows; with
+    ``block_sizes``, per pool block size (the inputs do not depend on it)."""
+    worst = {bs: {} for bs in (block_sizes or [None])}
+    for cfg, q, k, v in decode_inputs(cid, seed, rows, **over):
+        for bs in worst:
+            _fold(worst[bs], mistake_effects(q, k, v, bs or cfg["bs"], cfg["scale"]))
+    return worst if block_sizes else worst[None]
+
+
+def _long_rows(cid, seed, n=2, **over):
+    """The n shortest and n longest sequences of a long-context workload."""
+    ctx = build_scenario(cid, seed, **over).ctx
+    order = np.argsort(ctx)
+    return sorted({int(x) for x in list(order[:n]) + list(order[-n:])})
+
+
+SIGNAL_CASES = [
+    (2, 0, None), (2, 1, None), (2, 2, None),
+    (3, 0, None), (3, 1, None), (3, 2, None),
+    (4, 0, [0, 7, 8, 63]), (4, 1, [0, 7, 8, 63]), (4, 2, [0, 7, 8, 63]),
+    (5, 0, "long"), (5, 1, "long"), (5, 2, "long"),
+    (6, 0, None),
+]
+
+
+@pytest.mark.parametrize("cid,seed,rows", SIGNAL_CASES, ids=[f"cfg{c[0]}-seed{c[1]}" for c in SIGNAL_CASES])
+def test_signal_inputs_expose_every_block_head_and_new_token(cid, seed, rows):
+    """Config 3 at each pool block size it is specified over (8, 16, 32);
+    config 5: its two shortest and two longest sequences (the markers scale
+    with each sequence's length, so the effects do not grow or shrink with
+    it)."""
+    if rows == "long":
+        rows = _long_rows(cid, seed, signal=True)
+    sizes = [8, 16, 32] if cid == 3 else None
+    worst = _decode_worst(cid, seed, rows, block_sizes=sizes, signal=True)
+    for w in (worst.values() if sizes else [worst]):
+        for m in MISTAKES:
+            assert w[m] > TOL_BF16, (m, worst)
+
+
+def test_signal_inputs_expose_the_chunk_boundaries_and_diagonal():
+    """The mixed workload's 1,024-row chunk after 3,500 cached tokens: one
+    row at each end of every 256-row tile's position range (the rows the GPU
+    test checks include these), every block, the row's own key and the next
+    key (a causal mask one key off in either direction)."""
+    scn = build_scenario(5, 0, signal=True)
+    cfg, st = scn.cfg, scn.steps[0]
+    pf = st.prefill
+    k, v = scn.history(pf.seq, pf.ctx_before)
+    kc = np.concatenate([widen(k, "bf16"), widen(st.k_new[-pf.T:], "bf16")]).transpose(1, 0, 2)
+    vc = np.concatenate([widen(v, "bf16"), widen(st.v_new[-pf.T:], "bf16")]).transpose(1, 0, 2)
+    q = widen(pf.q, "bf16")
+    worst = {}
+    tp = 256 // cfg["G"]
+    for t in sorted({r for tile in range(0, pf.T, tp) for r in (tile, tile + tp - 1)})[::3]:
+        n = pf.ctx_before + t + 1
+        _fold(worst, mistake_effects(q[t], kc[:, :n], vc[:, :n], cfg["bs"], cfg["scale"]))
+        if t + 1 < pf.T:
+            a = attend(q[t], kc[:, :n], vc[:, :n], cfg["scale"])
+            b = attend(q[t], kc[:, :n + 1], vc[:, :n + 1], cfg["scale"])
+            _fold(worst, {"next_key": np.abs(a - b).max()})
+    for m in MISTAKES + ("next_key",):
+        assert worst[m] > TOL_BF16, (m, worst)
+
+
+@pytest.mark.parametrize("cid,over", [(2, {}), (4, {})])
+def test_plain_inputs_cannot_see_a_dropped_block(cid, over):
+    """Why the signal inputs exist: on the N(0,1) inputs some block of the
+    checked rows moves them by far less than the tolerance (a dropped block
+    there would pass).  A wrong KV head still shows."""
+    rows = [0, 7, 8, 63] if cid == 4 else None
+    worst = _decode_worst(cid, 0, rows, **over)
+    assert worst["drop_block"] < TOL_BF16 / 5
+    assert worst["wrong_head"] > TOL_BF16
+
+
+def test_block_effect_formula_matches_recomputation():
+    """The closed form for a dropped or duplicated block against attention
+    recomputed on K/V with that block removed or repeated."""
+    rng = np.random.default_rng(0)
+    H_q, H_kv, n, d, bs = 4, 2, 70, 16, 16
+    q = rng.standard_normal((H_q, d))
+    k = rng.standard_normal((H_kv, n, d))
+    v = rng.standard_normal((H_kv, n, d))
+    e = mistake_effects(q, k, v, bs, 0.3)
+    base = attend(q, k, v, 0.3)
+    drops, dups = [], []
+    for b in range(-(-n // bs)):
+        keep = np.r_[0:b * bs, min(n, (b + 1) * bs):n]
+        dd = attend(q, k[:, keep], v[:, keep], 0.3) - base
+        rep = np.r_[0:n, b * bs:min(n, (b + 1) * bs)]
+        du = attend(q, k[:, rep], v[:, rep], 0.3) - base
+        # per KV head: max over its query heads and dims
+        drops.append(np.abs(dd).reshape(H_kv, -1).max(axis=1))
+        dups.append(np.abs(du).reshape(H_kv, -1).max(axis=1))
+    assert np.isclose(e["drop_block"], np.min(drops), rtol=1e-9)
+    assert np.isclose(e["dup_block"], np.min(dups), rtol=1e-9)
+    dn = attend(q, k[:, :-1], v[:, :-1], 0.3) - base
+    assert np.isclose(e["drop_new"], np.abs(dn).reshape(H_kv, -1).max(axis=1).min(), rtol=1e-9)
+    wk = attend(q, np.roll(k, -1, axis=0), np.roll(v, -1, axis=0), 0.3) - base
+    assert np.isclose(e["wrong_head"], np.abs(wk).reshape(H_kv, -1).max(axis=1).min(), rtol=1e-9)
