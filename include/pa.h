@@ -241,13 +241,60 @@ int pa_mixed_batch(const pa_kv_pool* pool, int32_t layer, void* dec_out, const v
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decode attention of a batch whose sequences share leading blocks, reading
+ * each shared block once for all of its sharers.  Parallel sampling, beam
+ * search and common prompt prefixes leave several sequences whose block
+ * tables start with the same physical blocks, shared by reference count
+ * ([icarus] "支持块级共享"; [ttlab] "블록을 함께 쓰기"); pa_decode reads such
+ * a block once per sharer.  Same results as pa_decode (up to rounding
+ * order), for bf16 and f16 pools.
+ *   groups: host [n_groups], 0 <= n_groups <= 64, non-overlapping: rows
+ *        first_row .. first_row + n_rows - 1 of the batch all hold the same
+ *        physical blocks in their first shared_blocks table entries, and
+ *        each row's context covers them (shared_blocks * block_size <=
+ *        context_lens).  Rows in no group are decoded as pa_decode would.
+ *        The shared keys of a group run on the matrix cores for all its
+ *        rows and query heads at once; the rest of each row, and the
+ *        combination of the two, on the decode path.
+ *   workspace: device, 16-byte aligned, at least
+ *        pa_decode_shared_workspace_size(...) bytes (never 0 for B > 0).
+ *   Everything else as pa_decode.  Two launches (the decode, then a merge).
+ */
+typedef struct pa_share_group {
+  int32_t first_row;     /* first batch row of the group */
+  int32_t n_rows;        /* >= 1 consecutive rows */
+  int32_t shared_blocks; /* leading table entries all its rows share (>= 0) */
+} pa_share_group;
+
+size_t pa_decode_shared_workspace_size(const pa_kv_pool* pool, int32_t B, int32_t H_q, int32_t max_ctx,
+                                       const pa_share_group* groups, int32_t n_groups);
+int pa_decode_shared(const pa_kv_pool* pool, int32_t layer, void* out, const void* q, int32_t B, int32_t H_q,
+                     const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens, int32_t max_ctx,
+                     const pa_share_group* groups, int32_t n_groups, float scale, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Host helper for pa_decode_shared: scans a batch's host-side block tables
+ * ([B][max_blocks]) and context lengths ([B]) and returns the groups of
+ * consecutive rows (at least min_rows >= 2 of them) whose tables start
+ * with the same at least min_blocks >= 1 physical blocks, each fully inside
+ * every row's context.  Greedy, in row order: a run grows while its rows
+ * keep min_blocks common blocks, and shares as many as all of them hold.
+ *   out: host [cap]; *n_out = groups found.  PA_ESPACE if more than cap.
+ */
+int pa_share_groups(const int32_t* block_tables, int32_t B, int32_t max_blocks, const int32_t* context_lens,
+                    int32_t block_size, int32_t min_rows, int32_t min_blocks, pa_share_group* out, int32_t cap,
+                    int32_t* n_out);
+
+/*
  * Validate mode (for debugging): when on, every call above copies the device
  * indices it would trust to the host on its stream (synchronising it) and
  * returns PA_EINVAL, with nothing launched, if any is wrong -- a block id
  * outside [0, num_blocks) among a sequence's visible blocks, a context
  * length outside [0, max_ctx] or past its table, a slot out of range or
  * repeated, a fused append's slot that is not position context_lens - 1 of
- * its row, a copy pair out of range or whose destination is reused.  Off by
+ * its row, a copy pair out of range or whose destination is reused, a share group
+ * whose rows differ in their shared blocks or do not see all of them.  Off by
  * default; PA_VALIDATE=1 in the environment turns it on at load.  Not for
  * use under graph capture.  Returns the previous setting.
  */

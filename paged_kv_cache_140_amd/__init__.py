@@ -10,15 +10,19 @@ from .api import (  # noqa: F401
     BlockManager,
     KVPool,
     OutOfBlocks,
+    decode_shared_workspace,
     decode_workspace,
     pa_cache_append,
     pa_copy_blocks,
     pa_decode,
     pa_decode_append,
     pa_decode_noalloc,
+    pa_decode_shared,
+    pa_decode_shared_workspace_size,
     pa_decode_workspace_size,
     pa_mixed_batch,
     pa_set_tuning,
+    pa_share_groups,
     pa_set_validate,
     pa_sha256,
     pa_prefill_chunk,

@@ -39,6 +39,10 @@ _PPOOL = ctypes.POINTER(KVPoolStruct)
 class ChunkStruct(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("ctx_before", ctypes.c_int32)]
 
+class ShareGroupStruct(ctypes.Structure):
+    _fields_ = [("first_row", ctypes.c_int32), ("n_rows", ctypes.c_int32), ("shared_blocks", ctypes.c_int32)]
+
+
 SIGNATURES = {
     "pa_cache_append": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _p, _i32, _p]),
     "pa_copy_blocks": (ctypes.c_int, [_PPOOL, _p, _i32, _p]),
@@ -55,6 +59,13 @@ SIGNATURES = {
     "pa_mixed_batch": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _p, _p,
                                       ctypes.POINTER(ChunkStruct), _i32, _p, _i32, ctypes.c_float, _i32, _p,
                                       ctypes.c_size_t, _p]),
+    "pa_decode_shared_workspace_size": (ctypes.c_size_t, [_PPOOL, _i32, _i32, _i32,
+                                                          ctypes.POINTER(ShareGroupStruct), _i32]),
+    "pa_decode_shared": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _i32, _i32, _p, _i32, _p, _i32,
+                                        ctypes.POINTER(ShareGroupStruct), _i32, ctypes.c_float, _p, ctypes.c_size_t,
+                                        _p]),
+    "pa_share_groups": (ctypes.c_int, [_pi32, _i32, _i32, _pi32, _i32, _i32, _i32, ctypes.POINTER(ShareGroupStruct),
+                                       _i32, _pi32]),
     "pa_set_validate": (ctypes.c_int, [ctypes.c_int]),
     "pa_set_tuning": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -125,6 +125,61 @@ def pa_decode_noalloc(pool, layer, out, q, block_tables, context_lens, max_ctx, 
                                   _stream(stream)), "pa_decode_noalloc")
 
 
+def _groups_arg(groups):
+    groups = [(int(a), int(b), int(c)) for a, b, c in groups]
+    arr = (_lib.ShareGroupStruct * max(len(groups), 1))(*[_lib.ShareGroupStruct(*g) for g in groups])
+    return arr, len(groups)
+
+
+def pa_decode_shared_workspace_size(pool, B, H_q, max_ctx, groups):
+    arr, n = _groups_arg(groups)
+    s = pool.struct()
+    return int(lib().pa_decode_shared_workspace_size(ctypes.byref(s), int(B), int(H_q), int(max_ctx), arr, n))
+
+
+def decode_shared_workspace(pool, B, H_q, max_ctx, groups, device="cuda"):
+    """The workspace tensor pa_decode_shared needs for this batch and groups."""
+    n = pa_decode_shared_workspace_size(pool, B, H_q, max_ctx, groups)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def pa_decode_shared(pool, layer, out, q, block_tables, context_lens, max_ctx, scale, groups, workspace,
+                     stream=None):
+    """pa_decode for a batch whose rows share leading blocks: ``groups`` is a
+    list of (first_row, n_rows, shared_blocks)."""
+    B, H_q, d = (int(x) for x in q.shape)
+    _need(q, "q", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(out, "out", pool.torch_dtype, (B, H_q, pool.head_dim))
+    _need(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B][max_blocks]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    _need(workspace, "workspace")
+    arr, n = _groups_arg(groups)
+    s = pool.struct()
+    check(lib().pa_decode_shared(ctypes.byref(s), layer, _ptr(out), _ptr(q), B, H_q, _ptr(block_tables),
+                                 int(block_tables.shape[1]), _ptr(context_lens), int(max_ctx), arr, n, float(scale),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+          "pa_decode_shared")
+
+
+def pa_share_groups(block_tables, context_lens, block_size, min_rows=2, min_blocks=1):
+    """Groups of consecutive rows sharing leading full blocks, from host
+    tables (int32 [B][max_blocks]) and context lengths ([B]) -> list of
+    (first_row, n_rows, shared_blocks)."""
+    tab, tp = _arr(block_tables)
+    if tab.ndim != 2:
+        raise ValueError("block_tables must be [B][max_blocks]")
+    lens, lp = _arr(context_lens)
+    B, maxb = tab.shape
+    cap = max(B // 2, 1)
+    out = (_lib.ShareGroupStruct * cap)()
+    n = ctypes.c_int32(0)
+    check(lib().pa_share_groups(tp, B, maxb, lp, int(block_size), int(min_rows), int(min_blocks), out, cap,
+                                ctypes.byref(n)), "pa_share_groups")
+    return [(out[i].first_row, out[i].n_rows, out[i].shared_blocks) for i in range(n.value)]
+
+
 def pa_decode_append(pool, layer, out, q, k_new, v_new, slot_mapping, block_tables, context_lens, max_ctx, scale,
                      workspace=None, stream=None):
     """One decode step in one launch: append each sequence's new token

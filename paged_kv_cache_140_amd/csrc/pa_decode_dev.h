@@ -173,7 +173,14 @@ __device__ __forceinline__ void gather_heads(const uint32_t* own, uint32_t* all)
 // workgroup size would put one more memory round trip (which the scalar
 // wait counter cannot separate from the table loads) before the first K/V
 // loads.  smem holds W * G * (D + 2) floats.
-template <typename E, int D, int G, int BS, bool FUSED>
+//
+// SUFFIX: the part of a decode that follows the first skip_blocks blocks of
+// the sequence (a shared-prefix decode reads those for all its sharers at
+// once): partition ``part`` covers blocks skip_blocks + [part, part + 1) *
+// blocks_per_part, and the workgroup always writes (m, l, acc) partials,
+// which a merge combines with the prefix's; an empty partition writes
+// nothing.
+template <typename E, int D, int G, int BS, bool FUSED, bool SUFFIX = false>
 __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, int b, float* __restrict__ smem,
                                             char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off,
                                             int64_t head_stride, const char* __restrict__ q, void* __restrict__ out,
@@ -181,7 +188,9 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
                                             const int32_t* __restrict__ context_lens, float scale_log2, int32_t H_q,
                                             int32_t blocks_per_part, int32_t num_parts, float* __restrict__ ws_ml,
                                             float* __restrict__ ws_acc, const char* __restrict__ k_new,
-                                            const char* __restrict__ v_new, const int32_t* __restrict__ new_slots) {
+                                            const char* __restrict__ v_new, const int32_t* __restrict__ new_slots,
+                                            int skip_blocks = 0) {
+  static_assert(!(SUFFIX && FUSED), "a shared-prefix decode appends beforehand");
   using Sh = DecodeShape<E, D, BS, G>;
   constexpr int S = Sh::S, VEC = Sh::VEC, LPT = Sh::LPT, TPW = Sh::TPW, NLD = Sh::NLD, U = Sh::U, UPB = Sh::UPB,
                 RING = Sh::RING;
@@ -206,7 +215,7 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
   const int r = kScatter ? (lane / CLO) % TPW : lane / LPT;            // token row inside a wave load
   const int c = kScatter ? lane % CLO + CLO * (lane / 16) : lane % LPT;  // 16-byte chunk of the row
 
-  const int j0 = part * blocks_per_part;
+  const int j0 = (SUFFIX ? skip_blocks : 0) + part * blocks_per_part;
   const int u_begin = j0 * UPB;
   const int32_t* btrow = block_tables + static_cast<int64_t>(b) * max_blocks;
   // Table entries of this wave's first RING units, read in parallel with the
@@ -227,7 +236,7 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
     // Nothing visible in this partition.  With a single partition that means
     // an empty sequence: its rows are zeros.  Split partitions past the end
     // are not counted by the merge.
-    if (num_parts == 1) {
+    if (!SUFFIX && num_parts == 1) {
       for (int i = threadIdx.x; i < G * D; i += W * 64) store_elem(E{}, out, head0 * D + i, 0.0f);
     }
     return;
@@ -606,7 +615,7 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
       lt += sm_l[w * G + h] * wt;
       at += sm_acc[(w * G + h) * D + e] * wt;
     }
-    if (num_parts == 1) {
+    if (!SUFFIX && num_parts == 1) {
       store_elem(E{}, out, (head0 + h) * D + e, lt > 0.0f ? at / lt : 0.0f);
     } else {
       const int64_t slot = (head0 + h) * num_parts + part;

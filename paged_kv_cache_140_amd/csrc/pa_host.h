@@ -39,6 +39,9 @@ int check_pairs(const std::string& who, const pa_kv_pool* pool, const int32_t* p
 int check_decode_indices(const std::string& who, const pa_kv_pool* pool, int32_t B, const int32_t* block_tables,
                          int32_t max_blocks, const int32_t* context_lens, int32_t max_ctx, const int32_t* new_slots,
                          hipStream_t stream);
+int check_share_groups(const std::string& who, const pa_kv_pool* pool, int32_t B, const int32_t* block_tables,
+                       int32_t max_blocks, const int32_t* context_lens, const pa_share_group* groups, int32_t n_groups,
+                       hipStream_t stream);
 int check_prefill_indices(const std::string& who, const pa_kv_pool* pool, const int32_t* table, int32_t nb,
                           int32_t T, int32_t ctx_before, hipStream_t stream);
 

@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
       if (r > 0) __syncthreads();  // the previous item's output staging is read
       prefill_tile<E, D, G, BS>(w, lds, pool_k, pool_v, layer_off, head_stride, pq + rows, pout + rows,
                                 ptables + static_cast<int64_t>(ch.table_row[c]) * pt_stride, ch.T[c], H_q,
-                                ch.ctx_before[c], scale_log2, 0, INT32_MAX, nullptr, nullptr);
+                                ch.ctx_before[c], scale_log2, 0, INT32_MAX, nullptr, nullptr, INT32_MAX);
     }
     return;
   }

@@ -63,7 +63,8 @@ __global__ void __launch_bounds__(kPrefillThreads)
     wml = ws_ml + static_cast<int64_t>(split) * T * H_q * 2;
   }
   prefill_tile<E, D, G, BS>(w % items, lds, pool_k, pool_v, layer_off, head_stride, q, out, table, T, H_q,
-                            ctx_before, scale_log2, split * steps_per_split, (split + 1) * steps_per_split, wo, wml);
+                            ctx_before, scale_log2, split * steps_per_split, (split + 1) * steps_per_split, wo, wml,
+                            INT32_MAX);
 }
 
 // Combines the key splits of each chunk row (position, query head):

@@ -150,13 +150,18 @@ using PrefillLds = char[4][kKeysPerStep * D * 2];
 // [T][H_q][D] per split at ws_o) and (running max, sum) pairs ([T][H_q][2]
 // at ws_ml) instead of the output; a merge combines the splits.  Without a
 // split: step_lo = 0, step_hi >= every item's steps, ws_o = nullptr.
+//
+// key_end: no row sees key key_end or later (INT32_MAX for a chunk).  With
+// ctx_before >= key_end every row sees exactly the keys [0, key_end): the
+// shared-prefix pass of a decode, where the rows are the queries of the
+// sequences that share those keys' blocks.
 template <typename E, int D, int G, int BS>
 __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const char* __restrict__ pool_k,
                                              const char* __restrict__ pool_v, int64_t layer_off, int64_t head_stride,
                                              const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                                              const int32_t* __restrict__ table, int32_t T, int32_t H_q,
                                              int32_t ctx_before, float scale_log2, int step_lo, int step_hi,
-                                             float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+                                             float* __restrict__ ws_o, float* __restrict__ ws_ml, int32_t key_end) {
   using M = Mfma<E>;
   using vec = typename M::vec;
   constexpr int ROWS = kRowsPerWave * kPrefillWaves;  // query rows per workgroup
@@ -185,21 +190,26 @@ __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const ch
   const int li = lane & 31;
   const int h = lane >> 5;
   const int t_last = min(t0 + TP, T) - 1;
-  const int kmax = ctx_before + t_last + 1;  // no row of this workgroup sees key kmax or later
+  const int kmax = min(ctx_before + t_last + 1, key_end);  // no row of this workgroup sees key kmax or later
   // local steps 0 .. nsteps-1 are the item's 64-key steps s0 .. s0+nsteps-1
   const int s0 = step_lo;
   const int nsteps = min((kmax + KT - 1) / KT, step_hi) - s0;
   if (nsteps <= 0) return;  // uniform: this split holds none of the item's keys
-  const int first_masked_key = ctx_before + t0 + 1;
+  const int first_masked_key = min(ctx_before + t0 + 1, key_end);
   // Waves 0-3 (group A) and 4-7 (group B) share the SIMDs pairwise and run
   // the same work one phase apart.
   const bool group_b = wave >= kPrefillWaves / 2;
+  // A wave whose 32 rows all lie past the last row (a tile of few rows, such
+  // as a shared-prefix group's few sequences) has nothing to compute: it
+  // still issues its share of every tile load and meets every barrier, but
+  // skips its MFMA and softmax units.
+  const bool live = t0 + (wave * kRowsPerWave) / G < T;
 
   // This lane's query row (MFMA B operand: dims ks*16 + h*8 + [0,8)) and its
   // last visible key.
   const int r = wave * kRowsPerWave + li;
   const int pos = t0 + r / G;
-  const int limit = ctx_before + pos;
+  const int limit = min(ctx_before + pos, key_end - 1);
   vec qb[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -409,7 +419,7 @@ __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const ch
     barrier_keep_loads();
   }
   // gemm(-1): scores of step 0 only.
-  gemm(std::false_type{}, lds[0], lds[3]);
+  if (live) gemm(std::false_type{}, lds[0], lds[3]);
   if (!group_b) issue_round(0, lds[1], lds[2]);
   if (group_b) wait_loads_to_lds();
   barrier_keep_loads();
@@ -421,13 +431,13 @@ __device__ __forceinline__ void prefill_tile(int w, PrefillLds<D>& lds, const ch
   // compiler from waiting for these loads before them.
   auto softmax_unit = [&](int j, char* kb, char* vb) __attribute__((always_inline)) {
     if (group_b) issue_round(j + 1, kb, vb);
-    softmax(j);
+    if (live) softmax(j);
     if (!group_b) wait_loads_to_lds();
     barrier_keep_loads();
   };
   softmax_unit(0, lds[0], lds[3]);
   auto body = [&](int j, char* k_rd, char* v_rd, char* ka, char* va) __attribute__((always_inline)) {
-    gemm(std::true_type{}, k_rd, v_rd);
+    if (live) gemm(std::true_type{}, k_rd, v_rd);
     if (!group_b) issue_round(j, ka, va);
     if (group_b) wait_loads_to_lds();
     barrier_keep_loads();

@@ -101,6 +101,28 @@ int check_decode_indices(const std::string& who, const pa_kv_pool* pool, int32_t
   return PA_OK;
 }
 
+int check_share_groups(const std::string& who, const pa_kv_pool* pool, int32_t B, const int32_t* block_tables,
+                       int32_t max_blocks, const int32_t* context_lens, const pa_share_group* groups, int32_t n_groups,
+                       hipStream_t stream) {
+  std::vector<int32_t> lens, tab;
+  if (int e = fetch(who, context_lens, B, lens, stream)) return e;
+  if (int e = fetch(who, block_tables, static_cast<size_t>(B) * max_blocks, tab, stream)) return e;
+  for (int32_t c = 0; c < n_groups; ++c) {
+    const pa_share_group& g = groups[c];
+    const int32_t* t0 = tab.data() + static_cast<size_t>(g.first_row) * max_blocks;
+    for (int32_t r = g.first_row; r < g.first_row + g.n_rows; ++r) {
+      if (static_cast<int64_t>(g.shared_blocks) * pool->block_size > lens[r])
+        return fail(PA_EINVAL, who + ": group " + std::to_string(c) + " shares blocks row " + std::to_string(r) +
+                                   " does not fully see");
+      const int32_t* tr = tab.data() + static_cast<size_t>(r) * max_blocks;
+      for (int32_t j = 0; j < g.shared_blocks; ++j)
+        if (tr[j] != t0[j])
+          return fail(PA_EINVAL, who + ": group " + std::to_string(c) + " rows differ at block " + std::to_string(j));
+    }
+  }
+  return PA_OK;
+}
+
 int check_prefill_indices(const std::string& who, const pa_kv_pool* pool, const int32_t* table, int32_t nb,
                           int32_t T, int32_t ctx_before, hipStream_t stream) {
   std::vector<int32_t> tab;

@@ -13,8 +13,9 @@ import torch
 
 from pa_inputs import gen
 
-from .api import (BlockManager, KVPool, OutOfBlocks, TORCH_DTYPE, decode_workspace, pa_cache_append,
-                  pa_copy_blocks, pa_decode, pa_decode_append, pa_mixed_batch, pa_prefill_chunk, prefill_workspace)
+from .api import (BlockManager, KVPool, OutOfBlocks, TORCH_DTYPE, decode_shared_workspace, decode_workspace,
+                  pa_cache_append, pa_copy_blocks, pa_decode, pa_decode_append, pa_decode_shared, pa_mixed_batch,
+                  pa_prefill_chunk, pa_share_groups, prefill_workspace)
 
 
 def to_device(x, dtype, device):
@@ -42,6 +43,10 @@ class StepInputs:
     fusable: bool = False
     # launch row i of the decode holds the step's decode row order[i]
     order: object = None
+    # shared-prefix decode: groups of launch rows sharing leading blocks
+    # (first_row, n_rows, shared_blocks) and their workspace
+    groups: object = None
+    shared_ws: object = None
 
 
 class DeviceRun:
@@ -101,7 +106,7 @@ class DeviceRun:
                 raise ValueError(op)
 
     # -- one step ------------------------------------------------------------
-    def prepare(self, step, longest_first=False):
+    def prepare(self, step, longest_first=False, shared=False):
         """Host bookkeeping for ``step`` (its forks and frees, then its
         appends) and H2D staging of all its inputs.
 
@@ -111,7 +116,10 @@ class DeviceRun:
         bookkeeping stays in the step's order; only the decode's launch rows
         (tables, lengths, queries and, for a fused step, the new tokens and
         their slots) are permuted, and ``si.order[i]`` is the step row that
-        launch row i holds."""
+        launch row i holds.
+
+        ``shared``: also group the launch rows that share leading blocks
+        (pa_share_groups on the host tables) for pa_decode_shared."""
         cfg, dev = self.cfg, self.device
         for op in step.ops:
             if op[0] == "fork":
@@ -151,6 +159,10 @@ class DeviceRun:
                 if si.fusable:
                     si.k_new, si.v_new = si.k_new[pt].contiguous(), si.v_new[pt].contiguous()
                     si.slots = si.slots[pt].contiguous()
+                tables, lens = tables[perm], lens[perm]
+            if shared:
+                si.groups = pa_share_groups(tables, lens, cfg["bs"])
+                si.shared_ws = decode_shared_workspace(self.pool, len(lens), cfg["H_q"], max_ctx, si.groups, dev)
         if step.prefill is not None:
             pf = step.prefill
             table = np.array(self.bm.block_table(pf.seq), dtype=np.int32)
@@ -160,12 +172,14 @@ class DeviceRun:
         return si
 
     def launch(self, si, stream=None, do_copy=True, do_append=True, do_decode=True, do_prefill=True, fused=False,
-               mixed=False, prefill_workgroups=0):
+               mixed=False, prefill_workgroups=0, shared=False):
         """Enqueue the step's kernels in the contract order: copies, appends,
         attention.  ``fused``: a step that appends one token per decoded
         sequence runs its append and decode as one pa_decode_append.
         ``mixed``: a step with both a decode batch and a prefill chunk runs
-        the two attentions as one pa_mixed_batch."""
+        the two attentions as one pa_mixed_batch.  ``shared``: the decode
+        runs as pa_decode_shared over the groups ``prepare(shared=True)``
+        found."""
         cfg = self.cfg
         if mixed and do_decode and do_prefill and si.q is not None and si.prefill is not None:
             if do_copy and si.n_pairs:
@@ -185,14 +199,17 @@ class DeviceRun:
             do_append = do_decode = False
         if do_append and si.slots.numel():
             pa_cache_append(self.pool, self.layer, si.k_new, si.v_new, si.slots, stream)
-        if do_decode and si.q is not None:
+        if do_decode and si.q is not None and shared:
+            pa_decode_shared(self.pool, self.layer, si.out, si.q, si.tables, si.lens, si.max_ctx, cfg["scale"],
+                             si.groups, si.shared_ws, stream)
+        elif do_decode and si.q is not None:
             pa_decode(self.pool, self.layer, si.out, si.q, si.tables, si.lens, si.max_ctx, cfg["scale"],
                       si.workspace, stream)
         if do_prefill and si.prefill is not None:
             q, table, ctx_before, out, ws = si.prefill
             pa_prefill_chunk(self.pool, self.layer, out, q, table, ctx_before, cfg["scale"], ws, stream)
 
-    def run_step(self, step, fused=False, longest_first=False):
-        si = self.prepare(step, longest_first=longest_first)
-        self.launch(si, fused=fused)
+    def run_step(self, step, fused=False, longest_first=False, shared=False):
+        si = self.prepare(step, longest_first=longest_first, shared=shared)
+        self.launch(si, fused=fused, shared=shared)
         return si
