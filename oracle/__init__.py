@@ -21,6 +21,8 @@ Modules:
   pool           the physical block pool as bit patterns; append; block copy
   attention      gather through the block table; decode; causal prefill chunk
   run            drives a ``pa_inputs`` scenario through all of the above
+  capacity       KV slots that hold tokens, paged against max-length reservation
+  scheduler      chunked prefill: each step's prefill chunks under a token budget
 
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (printed examples, closed forms, invariants, torch's

@@ -26,6 +26,7 @@ import test_oracle_encoding as T_ENC  # noqa: E402
 import test_oracle_pool as T_POOL  # noqa: E402
 import test_oracle_prefix_cache as T_PC  # noqa: E402
 import test_oracle_run as T_RUN  # noqa: E402
+import test_oracle_scheduler as T_SCHED  # noqa: E402
 
 
 def plant(monkeypatch, module_name, old, new):
@@ -103,6 +104,9 @@ PC = [T_PC.test_key_is_sha256_of_previous_key_tokens_and_extra,
       T_PC.test_hits_on_live_blocks_share_them, T_PC.test_append_without_token_ids_stops_keying,
       T_PC.test_failed_append_changes_nothing, T_PC.test_identity_pool_fuzz]
 ADM = [T_PC.test_admission_queries_closed_forms, T_PC.test_admission_queries_equal_their_effect]
+SCHED = [T_SCHED.test_page_caps_on_a_3500_token_input, T_SCHED.test_decodes_count_against_the_budget,
+         T_SCHED.test_budget_below_the_decodes_leaves_no_prefill, T_SCHED.test_prompts_in_arrival_order_and_chunk_limit,
+         T_SCHED.test_brute_force_small_cases]
 CAP = [T_CAP.test_page_illustration, T_CAP.test_lognormal_lengths_waste_below_one_block,
        T_CAP.test_active_requests_in_the_page_pool, T_CAP.test_shared_blocks_count_once]
 RUN = [T_RUN.test_config1_paged_equals_logical_and_uses_12_blocks, T_RUN.test_config4_copy_on_write_pairs_small,
@@ -163,6 +167,13 @@ PLANTED = [
     ("admit-cost-ignores-waiting-hits", "oracle.block_manager", "            waiting += self.ref[b] == 0\n", "", ADM),
     ("admit-cost-ignores-hits", "oracle.block_manager",
      "return waiting + -(-len(tokens) // bs) - hits", "return waiting + -(-len(tokens) // bs)", ADM),
+    # chunked-prefill planner
+    ("decodes-not-counted", "oracle.scheduler", "left = budget - n_decode", "left = budget", SCHED),
+    ("chunk-ignores-budget", "oracle.scheduler", "t = min(rest, left)", "t = rest", SCHED),
+    ("chunk-restarts-at-zero", "oracle.scheduler", "out.append((i, done, t))", "out.append((i, 0, t))", SCHED),
+    ("no-chunk-limit", "oracle.scheduler", "if left <= 0 or len(out) == max_chunks:", "if left <= 0:", SCHED),
+    ("prompts-last-first", "oracle.scheduler", "for i, (length, done) in enumerate(prompts):",
+     "for i, (length, done) in reversed(list(enumerate(prompts))):", SCHED),
     # capacity
     ("shared-blocks-counted-twice", "oracle.capacity", "blocks = set()", "blocks = []", CAP),
     ("waste-off-by-one", "oracle.capacity", "return [len(bm.block_table(s)) * bm.block_size - bm.seq_len(s) for s in seqs]",
@@ -205,4 +216,4 @@ def test_planted_mistake_fails_a_pin(case, monkeypatch):
 
 
 def test_pins_pass_on_the_oracle_as_it_is():
-    assert first_failure(ATT + ENC + PC[:4] + ADM + CAP + RUN[:1] + POOL) is None
+    assert first_failure(ATT + ENC + PC[:4] + ADM + SCHED + CAP + RUN[:1] + POOL) is None
