@@ -409,6 +409,7 @@ def main():
                                "GBps": round(decode_bytes(L5, 8, 64, 128, 16, 2) / (ms_mix * 1e-3) / 1e9, 1),
                                "TFLOPs": round(fl / (ms_mix * 1e-3) / 1e12, 1)}
         rows["mixed_batch_4_chunks"] = four_chunk_row(torch, pa, np, g5, s5, fl)
+        rows["chunked_prefill_caps"] = chunked_prefill_row(torch, pa, np, g5, s5, ms_d5)
         del g5, s5
         torch.cuda.empty_cache()
         rows["prefix_cache"] = prefix_cache_row(torch, pa, np)
@@ -464,6 +465,47 @@ def four_chunk_row(torch, pa, np, g5, s5, fl_one):
                         "pa_prefill_chunk calls with their key-split workspaces",
             "ms": round(ms_mix, 5), "separate_ms": round(ms_sep, 5), "speedup": round(ms_sep / ms_mix, 3),
             "prefill_GFLOP": round(flops / 1e9, 1)}
+
+
+def chunked_prefill_row(torch, pa, np, g5, s5, ms_decode):
+    """The page's chunked-prefill measurement on this layer: a 3,500-token
+    prompt arrives while the 63 long-context sequences decode; pa_plan_step
+    cuts it under a per-step cap of 512 / 1,024 / 2,048 / 8,192 tokens (the
+    cap counts the 63 decode tokens too), and each step is one
+    pa_mixed_batch launch (the decodes + that step's chunk).  Per cap: the
+    steps, the slowest step (this layer's share of the longest gap between
+    two tokens of a running request) and the time until the prompt is
+    prefilled."""
+    cfg = g5.cfg
+    H_q, d, prompt = cfg["H_q"], cfg["d"], 3500
+    seq = 600000
+    g5.bm.add_seq(seq)
+    g5.bm.append_slots(seq, prompt)  # the pool already holds N(0,1) K/V everywhere
+    ptab = torch.tensor([g5.bm.block_table(seq)], dtype=torch.int32, device="cuda")
+    pq = torch.randn(prompt, H_q, d, device="cuda").to(torch.bfloat16)
+    pout = torch.empty_like(pq)
+    n_dec = int(s5.q.shape[0])
+    out = {"workload": "63 decodes of 1k-32k tokens (GQA 64/8) running while a 3,500-token prompt is prefilled in "
+                       "chunks; per cap: one pa_mixed_batch per step",
+           "decode_only_ms": round(ms_decode, 5)}
+    for cap in (512, 1024, 2048, 8192):
+        done, times, chunks = 0, [], []
+        while done < prompt:
+            (_, cb, T), = pa.pa_plan_step(cap, n_dec, [(prompt, done)])
+            r = slice(cb, cb + T)
+
+            def step(i, r=r, T=T, cb=cb):
+                pa.pa_mixed_batch(g5.pool, 0, s5.out, s5.q, s5.tables, s5.lens, s5.max_ctx, pout[r], pq[r],
+                                  [(T, cb)], ptab, cfg["scale"], 0, s5.workspace)
+
+            times.append(time_loop(torch, step, 3, 1))
+            chunks.append(T)
+            done = cb + T
+        out[str(cap)] = {"steps": len(times), "chunk_tokens": chunks, "max_step_ms": round(max(times), 5),
+                         "mean_step_ms": round(sum(times) / len(times), 5),
+                         "prompt_prefilled_ms": round(sum(times), 5)}
+    g5.bm.free_seq(seq)
+    return out
 
 
 def capacity_row(pa, np):

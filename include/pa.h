@@ -287,6 +287,36 @@ int pa_share_groups(const int32_t* block_tables, int32_t B, int32_t max_blocks, 
                     int32_t* n_out);
 
 /*
+ * Chunked prefill planning for pa_mixed_batch: a long prompt prefilled in
+ * one step stalls every running request's next token, so it is cut into
+ * chunks that share each step with the decodes, under a cap on the tokens a
+ * step processes ([ttlab] "3. 연속 배칭: 빈 자리를 걸음마다 채우기", part "새
+ * 문제: 긴 프리필이 디코드를 멈춘다").  The cap counts every token of the
+ * step: each of the n_decode running decodes takes one and is never
+ * postponed; the waiting prompts then take, in the given (arrival) order,
+ * chunks of their remaining prompt tokens until the cap is spent, at most
+ * max_chunks of them.  A prompt's chunk starts where its last one ended.
+ *   prompts: host [n_prompts], prompt_len >= computed >= 0 (prompt tokens
+ *            already prefilled).
+ *   out: host [max_chunks]; *n_out = chunks planned (0 when the decodes
+ *        fill the budget).  out[k] = (index into prompts, ctx_before = that
+ *        prompt's computed, T = tokens of this chunk), in prompt order: the
+ *        (T, ctx_before) pairs are pa_mixed_batch's chunk list.
+ * Host only; no state.  The caller advances each prompt's computed by T.
+ */
+typedef struct pa_prompt_state {
+  int32_t prompt_len;
+  int32_t computed;
+} pa_prompt_state;
+typedef struct pa_chunk_plan {
+  int32_t prompt;
+  int32_t ctx_before;
+  int32_t T;
+} pa_chunk_plan;
+int pa_plan_step(int32_t budget, int32_t n_decode, const pa_prompt_state* prompts, int32_t n_prompts,
+                 int32_t max_chunks, pa_chunk_plan* out, int32_t* n_out);
+
+/*
  * Validate mode (for debugging): when on, every call above copies the device
  * indices it would trust to the host on its stream (synchronising it) and
  * returns PA_EINVAL, with nothing launched, if any is wrong -- a block id

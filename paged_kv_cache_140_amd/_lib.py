@@ -43,6 +43,14 @@ class ShareGroupStruct(ctypes.Structure):
     _fields_ = [("first_row", ctypes.c_int32), ("n_rows", ctypes.c_int32), ("shared_blocks", ctypes.c_int32)]
 
 
+class PromptStateStruct(ctypes.Structure):
+    _fields_ = [("prompt_len", ctypes.c_int32), ("computed", ctypes.c_int32)]
+
+
+class ChunkPlanStruct(ctypes.Structure):
+    _fields_ = [("prompt", ctypes.c_int32), ("ctx_before", ctypes.c_int32), ("T", ctypes.c_int32)]
+
+
 SIGNATURES = {
     "pa_cache_append": (ctypes.c_int, [_PPOOL, _i32, _p, _p, _p, _i32, _p]),
     "pa_copy_blocks": (ctypes.c_int, [_PPOOL, _p, _i32, _p]),
@@ -66,6 +74,8 @@ SIGNATURES = {
                                         _p]),
     "pa_share_groups": (ctypes.c_int, [_pi32, _i32, _i32, _pi32, _i32, _i32, _i32, ctypes.POINTER(ShareGroupStruct),
                                        _i32, _pi32]),
+    "pa_plan_step": (ctypes.c_int, [_i32, _i32, ctypes.POINTER(PromptStateStruct), _i32, _i32,
+                                    ctypes.POINTER(ChunkPlanStruct), _pi32]),
     "pa_set_validate": (ctypes.c_int, [ctypes.c_int]),
     "pa_set_tuning": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),

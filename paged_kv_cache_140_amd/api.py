@@ -180,6 +180,19 @@ def pa_share_groups(block_tables, context_lens, block_size, min_rows=2, min_bloc
     return [(out[i].first_row, out[i].n_rows, out[i].shared_blocks) for i in range(n.value)]
 
 
+def pa_plan_step(budget, n_decode, prompts, max_chunks=32):
+    """One step's prefill chunks under a token budget (pa_plan_step):
+    prompts = [(prompt_len, computed)] in arrival order -> [(prompt index,
+    ctx_before, T)]."""
+    arr = (_lib.PromptStateStruct * max(len(prompts), 1))(
+        *[_lib.PromptStateStruct(int(n), int(c)) for n, c in prompts])
+    out = (_lib.ChunkPlanStruct * max(int(max_chunks), 1))()
+    n = ctypes.c_int32(0)
+    check(lib().pa_plan_step(int(budget), int(n_decode), arr, len(prompts), int(max_chunks), out, ctypes.byref(n)),
+          "pa_plan_step")
+    return [(out[i].prompt, out[i].ctx_before, out[i].T) for i in range(n.value)]
+
+
 def pa_decode_append(pool, layer, out, q, k_new, v_new, slot_mapping, block_tables, context_lens, max_ctx, scale,
                      workspace=None, stream=None):
     """One decode step in one launch: append each sequence's new token

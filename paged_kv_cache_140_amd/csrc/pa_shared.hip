@@ -100,16 +100,17 @@ __global__ void __launch_bounds__(kPrefillThreads)
 
 // Combines each (sequence, query head)'s partials: the prefix splits of its
 // group (if any) and the suffix partitions that hold some of its blocks:
-// out = sum_k o_k 2^(m_k - M) / sum_k l_k 2^(m_k - M), M = max_k m_k.  The
-// partials' weights are computed once, in LDS; each thread then sums its
-// dimension.
+// out = sum_k o_k 2^(m_k - M) / sum_k l_k 2^(m_k - M), M = max_k m_k.  Every
+// load is issued before any result is used -- each thread's first kPre
+// partial outputs and one partial's (m, l) -- so the merge waits for one
+// memory round trip; the weights go through LDS.
 template <typename E, int D>
 __global__ void __launch_bounds__(D)
     shared_merge_kernel(void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
                         const float* __restrict__ pre_o, const float* __restrict__ pre_ml,
                         const int32_t* __restrict__ context_lens, int32_t H_q, int32_t num_parts,
                         int32_t blocks_per_part, int32_t bs, GroupList gl) {
-  extern __shared__ float wt[];  // [max splits + num_parts] weights, then the total
+  extern __shared__ float wt[];  // [max splits + num_parts] weights
   __shared__ float red[2];
   const int64_t bh = blockIdx.x;
   const int b = static_cast<int>(bh / H_q);
@@ -122,26 +123,39 @@ __global__ void __launch_bounds__(D)
   const int ns = c >= 0 ? gl.splits[c] : 0;
   const int nblk = (context_lens[b] + bs - 1) / bs;
   const int np = max(0, min(num_parts, (nblk - skip + blocks_per_part - 1) / blocks_per_part));
+  const int nk = ns + np;
+  // partial k: prefix split k (k < ns) or suffix partition k - ns
   const int64_t prow0 = c >= 0 ? gl.row_off[c] + static_cast<int64_t>(b - gl.first_row[c]) * H_q + hd : 0;
   const int64_t pstride = c >= 0 ? static_cast<int64_t>(gl.n_rows[c]) * H_q : 0;  // rows per split
-  auto m_of = [&](int k) { return k < ns ? pre_ml[2 * (prow0 + k * pstride)] : ws_ml[2 * (bh * num_parts + k - ns)]; };
-  auto l_of = [&](int k) {
-    return k < ns ? pre_ml[2 * (prow0 + k * pstride) + 1] : ws_ml[2 * (bh * num_parts + k - ns) + 1];
-  };
-  auto o_of = [&](int k) { return k < ns ? pre_o[(prow0 + k * pstride) * D + e] : ws_acc[(bh * num_parts + k - ns) * D + e]; };
-  const int nk = ns + np;
-  float mx = kNegInf;
-  for (int k = e; k < nk; k += D) mx = fmaxf(mx, m_of(k));
+  auto row_of = [&](int k) { return k < ns ? prow0 + k * pstride : bh * num_parts + (k - ns); };
+  auto o_of = [&](int k) { return k < ns ? pre_o[row_of(k) * D + e] : ws_acc[row_of(k) * D + e]; };
+  constexpr int kPre = 16;
+  float pre[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) pre[i] = i < nk ? o_of(i) : 0.0f;
+  float2 ml = make_float2(kNegInf, 0.0f);
+  if (e < nk) {
+    const float* src = e < ns ? pre_ml : ws_ml;
+    ml = *reinterpret_cast<const float2*>(src + 2 * row_of(e));
+  }
+  float mx = ml.x;
+  for (int k = e + D; k < nk; k += D) mx = fmaxf(mx, (k < ns ? pre_ml : ws_ml)[2 * row_of(k)]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if ((e & 63) == 0) red[e >> 6] = mx;
   __syncthreads();
   mx = D > 64 ? fmaxf(red[0], red[1]) : red[0];
   const float ms = (mx == kNegInf) ? 0.0f : mx;
   float lsum = 0.0f;
-  for (int k = e; k < nk; k += D) {
-    const float w = exp2_fast(m_of(k) - ms);
+  if (e < nk) {
+    const float w = exp2_fast(ml.x - ms);
+    wt[e] = w;
+    lsum = ml.y * w;
+  }
+  for (int k = e + D; k < nk; k += D) {
+    const float* src = (k < ns ? pre_ml : ws_ml) + 2 * row_of(k);
+    const float w = exp2_fast(src[0] - ms);
     wt[k] = w;
-    lsum += l_of(k) * w;
+    lsum += src[1] * w;
   }
   for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
   __syncthreads();
@@ -149,12 +163,12 @@ __global__ void __launch_bounds__(D)
   __syncthreads();
   const float lt = D > 64 ? red[0] + red[1] : red[0];
   float a0 = 0.0f, a1 = 0.0f;
-  int k = 0;
-  for (; k + 1 < nk; k += 2) {
-    a0 += o_of(k) * wt[k];
-    a1 += o_of(k + 1) * wt[k + 1];
+#pragma unroll
+  for (int i = 0; i < kPre; i += 2) {
+    if (i < nk) a0 += pre[i] * wt[i];
+    if (i + 1 < nk) a1 += pre[i + 1] * wt[i + 1];
   }
-  if (k < nk) a0 += o_of(k) * wt[k];
+  for (int k = kPre; k < nk; ++k) a0 += o_of(k) * wt[k];
   store_elem(E{}, out, bh * D + e, lt > 0.0f ? (a0 + a1) / lt : 0.0f);
 }
 
