@@ -31,95 +31,174 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# Counter summary of the decode kernel on this workload (rocprofv3 FETCH_SIZE /
-# WRITE_SIZE passes, calibrated against a plain copy of known size).  Used only
-# while the kernel sources still hash to the value recorded with the counters.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b32_gqa16x8_ctx512-640_traffic.json")
-DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_140_amd", "csrc", f)
-                  for f in ("pa_decode.hip", "pa_decode_dev.h", "pa_common.h")]
-HEADLINE_KERNEL = "pa::decode_kernel<pa::BF16, 128, 2, 16, 1024, true>"
+CSRC = os.path.join(ROOT, "paged_kv_cache_140_amd", "csrc")
+# HBM bytes per launch of the counted kernels (rocprofv3 FETCH_SIZE /
+# WRITE_SIZE passes over this script, calibrated against a plain copy of
+# known size).  A kernel's figure is used only while its sources still hash
+# to the value recorded with the counters.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+SRC = {
+    "decode": ["pa_decode.hip", "pa_decode_dev.h", "pa_common.h"],
+    "shared": ["pa_shared.hip", "pa_decode_dev.h", "pa_prefill_dev.h", "pa_common.h"],
+    "cache": ["pa_cache.hip", "pa_common.h"],
+    "prefill": ["pa_prefill.hip", "pa_prefill_dev.h", "pa_common.h"],
+}
+# key: (kernel name as rocprofv3 prints it up to "(", grid size or None,
+# sources[, "unsplit": only dispatches not followed by a split's merge])
+COUNTED = {
+    "decode_b32_gqa16x8_fused": ("pa::decode_kernel<pa::BF16, 128, 2, 16, 1024, true>", None, "decode"),
+    "gather_b32_gqa16x8": ("pa::gather_kernel<pa::BF16, 128, 2, 16, 1024>", None, "decode"),
+    "decode_b64_mha40_bs16_fused": ("pa::decode_kernel<pa::BF16, 128, 1, 16, 1024, true>", None, "decode"),
+    "decode_b64_mha40_bs16": ("pa::decode_kernel<pa::BF16, 128, 1, 16, 1024, false>", None, "decode"),
+    "decode_b64_mha40_bs8": ("pa::decode_kernel<pa::BF16, 128, 1, 8, 1024, false>", None, "decode"),
+    "decode_b64_mha40_bs32": ("pa::decode_kernel<pa::BF16, 128, 1, 32, 1024, false>", None, "decode"),
+    "decode_shared_prefix_plain": ("pa::decode_kernel<pa::BF16, 128, 4, 16, 512, false>", None, "decode"),
+    "decode_shared_prefix_shared": ("pa::shared_decode_kernel<pa::BF16, 128, 4, 16>", None, "shared"),
+    "decode_long_ctx": ("pa::decode_kernel<pa::BF16, 128, 8, 16, 512, false>", None, "decode"),
+    "append_2048": ("pa::append_kernel", 524288, "cache"),
+    "copy_blocks_56": ("pa::copy_blocks_kernel", 229376, "cache"),
+    "prefill_chunk_1024": ("pa::prefill_chunk_kernel<pa::BF16, 128, 8, 16>", 131072, "prefill", "unsplit"),
+}
+HEADLINE = "decode_b32_gqa16x8_fused"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def sources_sha256(paths):
+def sources_sha256(names):
     import hashlib
 
     h = hashlib.sha256()
-    for p in paths:
-        with open(p, "rb") as f:
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per decode launch from the committed counter summary, or None
-    if there is none or the decode kernel changed since it was taken."""
+def recorded_traffic(key):
+    """HBM bytes per launch of a counted kernel from the committed counter
+    record, or None if there is none or its sources changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
-        rec = json.load(f)
-    if rec.get("source_sha256") != sources_sha256(DECODE_SOURCES):
+        rec = json.load(f).get("kernels", {}).get(key)
+    if not rec or rec.get("source_sha256") != sources_sha256(SRC[COUNTED[key][2]]):
         return None
     return rec.get("traffic_bytes_per_launch")
 
 
+def traffic_fields(key, algorithmic):
+    t = recorded_traffic(key)
+    return {"traffic_bytes": t, "traffic_over_algorithmic": round(t / algorithmic, 4) if t else None}
+
+
 def write_traffic_record(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
     """Turn two rocprofv3 counter runs of this script (``--pmc FETCH_SIZE``,
-    then ``--pmc WRITE_SIZE``, each ``-f csv``) into the traffic record that
-    ``roofline.traffic`` reports.  Each counter is summed over its instances
-    per dispatch and scaled by what it reads for the 512 MiB plain copy that
-    this script runs first (true size known)."""
+    then ``--pmc WRITE_SIZE``, each ``-f csv``) into the record the rows'
+    ``traffic`` fields come from.  Each counter is summed over its instances
+    per dispatch, the median dispatch of each counted kernel is taken, and
+    the counter is scaled by what it reads for the 512 MiB plain copy this
+    script runs first (true size known)."""
     import csv
     import glob
     import statistics
 
     def per_dispatch(d, counter):
         path = max(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True), key=os.path.getmtime)
-        acc, names = {}, {}
+        acc, meta = {}, {}
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
                 k = int(r["Dispatch_Id"])
                 acc[k] = acc.get(k, 0.0) + float(r["Counter_Value"])
-                names[k] = r["Kernel_Name"]
-        return acc, names
+                meta[k] = (r["Kernel_Name"], int(r["Grid_Size"]))
+        return acc, meta
 
-    fetch, fnames = per_dispatch(fetch_dir, "FETCH_SIZE")
-    write, wnames = per_dispatch(write_dir, "WRITE_SIZE")
+    def short(n):
+        return n.split("(")[0].replace("void ", "").strip()
+
+    def pick(acc, meta, name, grid, unsplit=False):
+        ids = sorted(meta)
+        nxt = {a: short(meta[b][0]) for a, b in zip(ids, ids[1:])}
+        return [v for k, v in acc.items()
+                if short(meta[k][0]) == name and (grid is None or meta[k][1] == grid)
+                and not (unsplit and "merge_kernel" in nxt.get(k, ""))]
+
+    fetch, fmeta = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, wmeta = per_dispatch(write_dir, "WRITE_SIZE")
     copy_kib = (512 << 20) / 1024
-    f_copy = max(v for k, v in fetch.items() if COPY_KERNEL in fnames[k])
-    w_copy = max(v for k, v in write.items() if COPY_KERNEL in wnames[k])
+    f_copy = max(pick(fetch, fmeta, COPY_KERNEL, None))
+    w_copy = max(pick(write, wmeta, COPY_KERNEL, None))
     f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
-    f_head = statistics.median(v for k, v in fetch.items() if HEADLINE_KERNEL + "(" in fnames[k])
-    w_head = statistics.median(v for k, v in write.items() if HEADLINE_KERNEL + "(" in wnames[k])
-    n = sum(1 for k in fetch if HEADLINE_KERNEL + "(" in fnames[k])
-    traffic = int(round((f_head * f_scale + w_head * w_scale) * 1024))
-    algorithmic = 75289232
+    kernels = {}
+    for key, (name, grid, src, *flags) in COUNTED.items():
+        unsplit = "unsplit" in flags
+        fv, wv = pick(fetch, fmeta, name, grid, unsplit), pick(write, wmeta, name, grid, unsplit)
+        if not fv or not wv:
+            continue
+        f_med, w_med = statistics.median(fv), statistics.median(wv)
+        kernels[key] = {
+            "kernel": name, "grid_size": grid, "dispatches": len(fv),
+            "fetch_size_kib_per_dispatch_median": f_med, "write_size_kib_per_dispatch_median": w_med,
+            "fetch_bytes_per_launch": int(round(f_med * f_scale * 1024)),
+            "write_bytes_per_launch": int(round(w_med * w_scale * 1024)),
+            "traffic_bytes_per_launch": int(round((f_med * f_scale + w_med * w_scale) * 1024)),
+            "source_sha256": sources_sha256(SRC[src]), "sources": SRC[src]}
     rec = {
-        "kernel": HEADLINE_KERNEL + " (pa_decode_append: append + decode)",
-        "workload": "B=32, GQA 16/8, head_dim 128, block 16, ctx U[512,640]+1, seed 0, 28 layers rotated; one new "
-                    "token per sequence appended in the same launch",
+        "what": "HBM bytes per launch of each counted kernel on this script's workloads (median dispatch)",
         "commands": [
-            f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -- python bench.py --no-cpu-baseline --no-rows",
-            f"rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -- python bench.py --no-cpu-baseline --no-rows",
+            f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o run -- python3 bench.py --steps 20 --warmup 5 "
+            "--no-cpu-baseline",
+            f"rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o run -- python3 bench.py --steps 20 --warmup 5 "
+            "--no-cpu-baseline",
             f"python bench.py --traffic-record {fetch_dir} {write_dir}",
         ],
-        "dispatches": n,
-        "fetch_size_kib_per_dispatch_median": f_head,
-        "write_size_kib_per_dispatch_median": w_head,
         "calibration": {"kernel": COPY_KERNEL + " (torch copy of 512 MiB, run first by bench.py)",
                         "fetch_size_kib": f_copy, "write_size_kib": w_copy, "true_kib": copy_kib,
                         "fetch_scale": f_scale, "write_scale": w_scale},
-        "traffic_bytes_per_launch": traffic,
-        "algorithmic_bytes_per_launch": algorithmic,
-        "traffic_over_algorithmic": round(traffic / algorithmic, 4),
-        "source_sha256": sources_sha256(DECODE_SOURCES),
-        "sources": [os.path.relpath(p, ROOT) for p in DECODE_SOURCES],
+        "kernels": kernels,
     }
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
-    print(json.dumps(rec))
+    print(json.dumps({k: v["traffic_bytes_per_launch"] for k, v in kernels.items()}))
+
+
+def write_trace_summary(trace_dir, out_path=os.path.join(ROOT, "profiles", "bench_kernel_trace_stats.md")):
+    """Summarise a ``rocprofv3 --kernel-trace --stats -f csv`` run of this
+    script: per kernel (name and grid), dispatches and median / mean / min
+    duration from the trace, next to the tool's own stats."""
+    import csv
+    import glob
+    import statistics
+
+    path = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+    by = {}
+    with open(path) as f:
+        recs = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    for i, r in enumerate(recs):
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+        if not name.startswith("pa::"):
+            continue
+        grid = int(r["Grid_Size"]) if "Grid_Size" in r else \
+            int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        if name.startswith("pa::prefill_chunk_kernel") and i + 1 < len(recs) and \
+                "prefill_merge_kernel" in recs[i + 1]["Kernel_Name"]:
+            name += " (split; merge follows)"
+        key = (name, grid)
+        by.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    lines = ["# rocprofv3 kernel trace of bench.py", "",
+             "Command (from the repository root; `cd /tmp && export TMPDIR=/tmp` first):", "",
+             f"    rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o run -- python3 bench.py --steps 20 "
+             "--warmup 5 --no-cpu-baseline",
+             f"    python bench.py --trace-summary {trace_dir}", "",
+             "Durations in us, per kernel and grid size; eager warm-up dispatches included (the bench's own "
+             "figures time graph replays after warm-up).", "",
+             "| kernel | grid | dispatches | median | mean | min |", "|---|---|---|---|---|---|"]
+    for (name, grid), d in sorted(by.items(), key=lambda x: -sum(x[1])):
+        lines.append(f"| `{name}` | {grid} | {len(d)} | {statistics.median(d):.2f} | {statistics.mean(d):.2f} | "
+                     f"{min(d):.2f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out_path)
 
 
 def parse():
@@ -134,7 +213,9 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=512,
                     help="size of a plain device copy run once before timing (counter calibration)")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the decode traffic record from two rocprofv3 counter runs, then exit (no GPU)")
+                    help="write the traffic record from two rocprofv3 counter runs, then exit (no GPU)")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="write profiles/bench_kernel_trace_stats.md from a rocprofv3 trace run, then exit (no GPU)")
     return ap.parse_args()
 
 
@@ -159,6 +240,37 @@ def prefill_flops(T, H_q, d, ctx_before):
 
 
 # ------------------------------------------------------------------ timing
+
+def time_replays(torch, fn, iters, warmup, replays):
+    """Sorted ms per call of each of ``replays`` timed replays (see time_loop)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(warmup + i)
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / iters)
+    del g
+    return sorted(times)
+
+
+def spread(times):
+    """median, p10 and p90 of per-replay times (nearest rank)."""
+    n = len(times)
+    return {"median": round(times[n // 2], 5), "p10": round(times[int(0.1 * (n - 1) + 0.5)], 5),
+            "p90": round(times[int(0.9 * (n - 1) + 0.5)], 5), "replays": n}
+
 
 def time_loop(torch, fn, iters, warmup, replays=5):
     """Average ms per call of fn(i) over ``iters`` consecutive calls.
@@ -196,6 +308,9 @@ def main():
     args = parse()
     if args.traffic_record:
         write_traffic_record(*args.traffic_record)
+        return 0
+    if args.trace_summary:
+        write_trace_summary(args.trace_summary)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -256,10 +371,39 @@ def main():
         gpu.launch(si, do_decode=False, do_prefill=False)
 
     assert si.fusable and si.n_pairs == 0  # the step is exactly one fused launch
-    ms_step = time_loop(torch, full_step, args.steps, args.warmup)
+    step_times = time_replays(torch, full_step, args.steps, args.warmup, 11)
+    ms_step = step_times[len(step_times) // 2]
     ms_unfused = time_loop(torch, unfused_step, args.steps, args.warmup)
-    ms_decode = time_loop(torch, decode_only, args.steps, args.warmup)
+    decode_times = time_replays(torch, decode_only, args.steps, args.warmup, 11)
+    ms_decode = decode_times[len(decode_times) // 2]
     ms_append = time_loop(torch, append_only, args.steps, args.warmup)
+
+    # Gather ceiling: pa_decode's own grid, tables, unit walk and loads with
+    # no arithmetic (pa_gather_checksum), on the same layers; and the same
+    # walk over tables that place each sequence's blocks back to back.
+    B2 = len(lens)
+    cs_buf = torch.empty(max(pa.pa_gather_checksum_size(gpu.pool, B2, cfg["H_q"], si.max_ctx) // 4, 1),
+                         dtype=torch.int32, device=dev)
+
+    def gather_scattered(i):
+        pa.pa_gather_checksum(gpu.pool, i % L, cfg["H_q"], si.tables, si.lens, si.max_ctx, cs_buf)
+
+    nblk = [-(-int(n) // cfg["bs"]) for n in lens]
+    contig = np.zeros(tuple(si.tables.shape), dtype=np.int32)
+    off = 0
+    for r_, nb in enumerate(nblk):
+        contig[r_, :nb] = np.arange(off, off + nb)
+        off += nb
+    assert off <= cfg["num_blocks"]
+    contig_d = torch.from_numpy(contig).to(dev)
+
+    def gather_contiguous(i):
+        pa.pa_gather_checksum(gpu.pool, i % L, cfg["H_q"], contig_d, si.lens, si.max_ctx, cs_buf)
+
+    gather_times = time_replays(torch, gather_scattered, args.steps, args.warmup, 11)
+    ms_gather = gather_times[len(gather_times) // 2]
+    ms_gather_c = time_loop(torch, gather_contiguous, args.steps, args.warmup)
+    gbytes = dbytes - 2 * B2 * cfg["H_q"] * cfg["d"] * s  # K/V and tables: what the walk reads
     value = dbytes / (ms_step * 1e-3) / 1e9
     kernel_bytes = dbytes + abytes  # the fused kernel also reads the new rows and writes them into the pool
     achieved = kernel_bytes / (ms_step * 1e-3) / 1e9
@@ -289,6 +433,20 @@ def main():
         "timing": "HIP graph of K steps replayed 5 times after W eager warmup steps and one untimed replay; "
                   "each replay timed with events, the median replay reported",
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "step_ms_spread": spread(step_times),
+        "decode_ms_spread": spread(decode_times),
+        "gather_ceiling": {
+            "what": "pa_gather_checksum: the decode's grid, block tables, unit walk and K/V loads, every loaded dword "
+                    "XORed into a checksum, no softmax; same layers rotated, same timing",
+            "scattered_ms": round(ms_gather, 5),
+            "scattered_GBps": round(gbytes / (ms_gather * 1e-3) / 1e9, 1),
+            "scattered_spread": spread(gather_times),
+            "contiguous_tables_ms": round(ms_gather_c, 5),
+            "contiguous_tables_GBps": round(gbytes / (ms_gather_c * 1e-3) / 1e9, 1),
+            "decode_over_ceiling": round(ms_gather / ms_decode, 4),
+            "step_over_ceiling": round(ms_gather / ms_step, 4),
+            "ceiling_hbm_frac": round(gbytes / (ms_gather * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            **traffic_fields("gather_b32_gqa16x8", gbytes)},
         "unfused_step_ms": round(ms_unfused, 5),
         "decode_ms": round(ms_decode, 5),
         "append_ms": round(ms_append, 5),
@@ -301,7 +459,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(),
+            "traffic": recorded_traffic(HEADLINE),
             "kernel": "pa::decode_kernel<BF16,128,2,16,1024> (pa_decode_append: append + decode)",
             "per_launch_bytes": kernel_bytes,
         },
@@ -325,12 +483,16 @@ def main():
     lens3 = si3.lens.cpu().numpy()
     b3 = decode_bytes(lens3, 40, 40, 128, 16, 2)
     out["attention_tok_s_b64"] = round(64 / (ms3 * 1e-3), 1)
+    a3 = append_bytes(64, 40, 128, 2)
     out["b64"] = {"workload": "13b-shaped MHA decode layer, B=64, 40 heads, block 16, lognormal ctx, churned pool; "
                               "append + decode in one launch, batch submitted longest context first",
                   "ms_per_step": round(ms3, 5), "decode_ms": round(ms3d, 5),
                   "decode_GBps": round(b3 / (ms3d * 1e-3) / 1e9, 1),
+                  "decode_hbm_frac": round(b3 / (ms3d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "step_GBps": round(b3 / (ms3 * 1e-3) / 1e9, 1),
-                  "batch_order_ms_per_step": round(ms3_batch, 5)}
+                  "batch_order_ms_per_step": round(ms3_batch, 5),
+                  "step_traffic": traffic_fields("decode_b64_mha40_bs16_fused", b3 + a3),
+                  "decode_traffic": traffic_fields("decode_b64_mha40_bs16", b3)}
     del g3, si3, si3b
     torch.cuda.empty_cache()
     # the same workload at the other block sizes it is specified over
@@ -345,7 +507,8 @@ def main():
         ms_d = time_loop(torch, lambda i: g_bs.launch(si_bs, do_copy=False, do_append=False), n3, 5)
         b_bs = decode_bytes(si_bs.lens.cpu().numpy(), 40, 40, 128, bs, 2)
         sweep[str(bs)] = {"ms_per_step": round(ms_f, 5), "decode_ms": round(ms_d, 5),
-                          "decode_GBps": round(b_bs / (ms_d * 1e-3) / 1e9, 1)}
+                          "decode_GBps": round(b_bs / (ms_d * 1e-3) / 1e9, 1),
+                          "decode_traffic": traffic_fields(f"decode_b64_mha40_bs{bs}", b_bs)}
         del g_bs, si_bs
         torch.cuda.empty_cache()
     out["b64"]["block_size_sweep"] = {k: sweep[k] for k in ("8", "16", "32")}
@@ -367,10 +530,12 @@ def main():
         copy_b = 2 * tail.n_pairs * 1 * 2 * 8 * 16 * 128 * 2
         uniq = 8 * 3000 * 8 * 128 * 2 * 2 + 64 * (int(L4[0]) - 3000) * 8 * 128 * 2 * 2
         rows["cow_copy_blocks"] = {"workload": "shared-prefix sampling: 56 copy-on-write block copies",
-                                   "ms": round(ms_copy, 5), "GBps": round(copy_b / (ms_copy * 1e-3) / 1e9, 1)}
+                                   "ms": round(ms_copy, 5), "GBps": round(copy_b / (ms_copy * 1e-3) / 1e9, 1),
+                                   **traffic_fields("copy_blocks_56", copy_b)}
         rows["append_2048"] = {"workload": "shared-prefix sampling: 64 x 32-token tails",
                                "ms": round(ms_tail, 5),
-                               "GBps": round(append_bytes(2048, 8, 128, 2) / (ms_tail * 1e-3) / 1e9, 1)}
+                               "GBps": round(append_bytes(2048, 8, 128, 2) / (ms_tail * 1e-3) / 1e9, 1),
+                               **traffic_fields("append_2048", append_bytes(2048, 8, 128, 2))}
         rows["decode_shared_prefix"] = {
             "workload": "64 samples sharing 8 x 3,000-token prefixes, ctx 3,034; pa_decode_shared (8 groups of 8 "
                         "rows sharing 187 blocks, read once per group) against pa_decode (read once per sample)",
@@ -381,7 +546,10 @@ def main():
             "groups": [list(g_) for g_ in dec.groups],
             "pa_decode_ms": round(ms_d4, 5),
             "pa_decode_unique_GBps": round(uniq / (ms_d4 * 1e-3) / 1e9, 1),
-            "speedup": round(ms_d4 / ms_d4s, 3)}
+            "speedup": round(ms_d4 / ms_d4s, 3),
+            "unique_bytes": uniq,
+            "traffic_over_unique": traffic_fields("decode_shared_prefix_shared", uniq),
+            "pa_decode_traffic_over_unique": traffic_fields("decode_shared_prefix_plain", uniq)}
         del g4, tail, dec
         torch.cuda.empty_cache()
 
@@ -395,11 +563,18 @@ def main():
         fl = prefill_flops(1024, 64, 128, 3500)
         rows["decode_long_ctx"] = {"workload": "63 sequences, ctx U[1024, 32768], GQA 64/8, submitted longest first",
                                    "ms": round(ms_d5, 5),
-                                   "GBps": round(decode_bytes(L5, 8, 64, 128, 16, 2) / (ms_d5 * 1e-3) / 1e9, 1)}
+                                   "GBps": round(decode_bytes(L5, 8, 64, 128, 16, 2) / (ms_d5 * 1e-3) / 1e9, 1),
+                                   "hbm_frac": round(decode_bytes(L5, 8, 64, 128, 16, 2) / (ms_d5 * 1e-3) / 1e9
+                                                     / HBM_PEAK_GBS, 4),
+                                   "decode_tok_s": round(63 / (ms_d5 * 1e-3), 1),
+                                   **traffic_fields("decode_long_ctx", decode_bytes(L5, 8, 64, 128, 16, 2))}
         rows["prefill_chunk"] = {"workload": "1,024-token causal chunk after 3,500 cached tokens, GQA 64/8",
                                  "ms": round(ms_p5, 5),
                                  "TFLOPs": round(fl / (ms_p5 * 1e-3) / 1e12, 1),
-                                 "mfma_frac": round(fl / (ms_p5 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+                                 "mfma_frac": round(fl / (ms_p5 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                                 "prefill_tok_s": round(1024 / (ms_p5 * 1e-3), 1),
+                                 **traffic_fields("prefill_chunk_1024", 1024 * 64 * 128 * 2 * 2 +
+                                                  (3500 + 1024) * 8 * 128 * 2 * 2)}
         ms_sep = time_loop(torch, lambda i: g5.launch(s5, do_copy=False, do_append=False), 10, 2)
         ms_mix = time_loop(torch, lambda i: g5.launch(s5, do_copy=False, do_append=False, mixed=True), 10, 2)
         rows["mixed_batch"] = {"workload": "the 63 decodes and the 1,024-token chunk as one pa_mixed_batch launch "
@@ -619,11 +794,43 @@ def cpu_baseline(seconds, dbytes):
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
+    one = {}
+    with threadpool_limits(limits=1):
+        for cid, secs in ((1, 1.0), (2, 3.0)):
+            one[f"config{cid}_ms_per_step"] = round(oracle_step_ms(cid, secs), 3)
     return {"value": round(dbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"the same decode step (append 32 + decode 32 sequences, float64 oracle) repeated {reps} "
                       f"times in {el:.1f} s on {cores} visible host cores",
-            "ms_per_step": round(1e3 * el / reps, 3)}
+            "ms_per_step": round(1e3 * el / reps, 3),
+            "one_thread": dict(one, sample="the tiny fp32 step (4 sequences) and the same B=32 step, each repeated "
+                                           "for ~1 s / ~3 s with BLAS limited to one thread")}
+
+
+def oracle_step_ms(cid, seconds):
+    """ms per append + decode step of workload ``cid`` in the oracle."""
+    from oracle import attention, encoding
+    from oracle.run import OracleRun, widen
+    from pa_inputs import build_scenario
+
+    scn = build_scenario(cid, 0)
+    orc = OracleRun(scn)
+    orc.run_setup()
+    st = scn.steps[0]
+    slots, _ = orc.bookkeeping(st)
+    cfg = scn.cfg
+    kb, vb = encoding.encode(st.k_new, cfg["dtype"]), encoding.encode(st.v_new, cfg["dtype"])
+    q = widen(st.q, cfg["dtype"])
+    tables = [orc.bm.block_table(s_) for s_ in st.decode_seqs]
+    lens = [orc.bm.seq_len(s_) for s_ in st.decode_seqs]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.pool.append(0, kb, vb, slots)
+        attention.decode(orc.pool, 0, q, tables, lens, cfg["scale"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return 1e3 * el / reps
 
 
 if __name__ == "__main__":

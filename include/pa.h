@@ -174,6 +174,25 @@ int pa_decode_noalloc(const pa_kv_pool* pool, int32_t layer, void* out, const vo
                       float scale, hipStream_t stream);
 
 /*
+ * A measuring aid, not part of the hot path: pa_decode's grid, block-table
+ * reads, unit walk and K/V loads, without the arithmetic.  Every loaded
+ * 16-byte chunk of K and V is XORed into one uint32 per wave.  What
+ * pa_decode's access pattern alone can stream; a benchmark states the
+ * decode's rate as a fraction of this one.  bf16 pools, head_dim 64 or 128.
+ *   checksums: device uint32, at least pa_gather_checksum_size(...) bytes;
+ *        entry ((b * P + p) * H_kv + g) * W + w is wave w of partition p
+ *        of (sequence b, KV head g) (P partitions, W waves: pa_decode's
+ *        plan).  The XOR of a (b, g)'s entries is the XOR of the K and V
+ *        dwords of every token of the units its waves read (every visible
+ *        token; at a partly filled last unit, its whole unit).
+ *   Everything else as pa_decode (no q, no out, no workspace).
+ */
+size_t pa_gather_checksum_size(const pa_kv_pool* pool, int32_t B, int32_t H_q, int32_t max_ctx);
+int pa_gather_checksum(const pa_kv_pool* pool, int32_t layer, int32_t B, int32_t H_q, const int32_t* block_tables,
+                       int32_t max_blocks, const int32_t* context_lens, int32_t max_ctx, uint32_t* checksums,
+                       size_t checksum_bytes, hipStream_t stream);
+
+/*
  * Workspace bytes pa_prefill_chunk can use to split a chunk over its keys
  * (0 when it would not split).  Depends on host-side sizes and the current
  * device's CU count only.

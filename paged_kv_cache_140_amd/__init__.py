@@ -25,6 +25,8 @@ from .api import (  # noqa: F401
     pa_share_groups,
     pa_set_validate,
     pa_sha256,
+    pa_gather_checksum,
+    pa_gather_checksum_size,
     pa_plan_step,
     pa_prefill_chunk,
     pa_prefill_workspace_size,

@@ -76,6 +76,8 @@ SIGNATURES = {
                                        _i32, _pi32]),
     "pa_plan_step": (ctypes.c_int, [_i32, _i32, ctypes.POINTER(PromptStateStruct), _i32, _i32,
                                     ctypes.POINTER(ChunkPlanStruct), _pi32]),
+    "pa_gather_checksum_size": (ctypes.c_size_t, [_PPOOL, _i32, _i32, _i32]),
+    "pa_gather_checksum": (ctypes.c_int, [_PPOOL, _i32, _i32, _i32, _p, _i32, _p, _i32, _p, ctypes.c_size_t, _p]),
     "pa_set_validate": (ctypes.c_int, [ctypes.c_int]),
     "pa_set_tuning": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),

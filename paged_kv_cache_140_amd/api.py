@@ -180,6 +180,28 @@ def pa_share_groups(block_tables, context_lens, block_size, min_rows=2, min_bloc
     return [(out[i].first_row, out[i].n_rows, out[i].shared_blocks) for i in range(n.value)]
 
 
+def pa_gather_checksum_size(pool, B, H_q, max_ctx):
+    s = pool.struct()
+    return int(lib().pa_gather_checksum_size(ctypes.byref(s), int(B), int(H_q), int(max_ctx)))
+
+
+def pa_gather_checksum(pool, layer, H_q, block_tables, context_lens, max_ctx, checksums=None, stream=None):
+    """pa_decode's walk and loads without the arithmetic (a measuring aid):
+    returns the uint32 checksum tensor ([B][P][H_kv][W] per-wave XORs)."""
+    B = int(context_lens.shape[0])
+    _need(block_tables, "block_tables", torch.int32)
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    s = pool.struct()
+    n = int(lib().pa_gather_checksum_size(ctypes.byref(s), B, int(H_q), int(max_ctx)))
+    if checksums is None:
+        checksums = torch.empty(max(n // 4, 1), dtype=torch.int32, device=block_tables.device)
+    check(lib().pa_gather_checksum(ctypes.byref(s), layer, B, int(H_q), _ptr(block_tables),
+                                   int(block_tables.shape[1]), _ptr(context_lens), int(max_ctx), _ptr(checksums),
+                                   checksums.numel() * checksums.element_size(), _stream(stream)),
+          "pa_gather_checksum")
+    return checksums
+
+
 def pa_plan_step(budget, n_decode, prompts, max_chunks=32):
     """One step's prefill chunks under a token budget (pa_plan_step):
     prompts = [(prompt_len, computed)] in arrival order -> [(prompt index,

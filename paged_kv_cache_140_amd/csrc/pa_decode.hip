@@ -69,6 +69,27 @@ __global__ void __launch_bounds__(MAXT)
                                   blocks_per_part, num_parts, ws_ml, ws_acc, k_new, v_new, new_slots);
 }
 
+// pa_decode's walk without the arithmetic: the same grid, tables, unit
+// order and loads, every loaded dword XORed into a per-wave checksum.
+template <typename E, int D, int G, int BS, int MAXT>
+__global__ void __launch_bounds__(MAXT)
+    gather_kernel(char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off, int64_t head_stride,
+                  const int32_t* __restrict__ block_tables, int32_t max_blocks,
+                  const int32_t* __restrict__ context_lens, int32_t H_q, int32_t blocks_per_part, int32_t num_parts,
+                  int32_t waves, uint32_t* __restrict__ checksums) {
+  extern __shared__ float smem[];
+  int part = blockIdx.y;
+  if (num_parts >= 4) {
+    part += blockIdx.z & 3;
+    if (part >= num_parts) part -= num_parts;
+  }
+  decode_body<E, D, G, BS, false, false, true>(waves, blockIdx.x, part, gridDim.x, blockIdx.z, smem, pool_k, pool_v,
+                                               layer_off, head_stride, nullptr, nullptr, block_tables, max_blocks,
+                                               context_lens, 0.0f, H_q, blocks_per_part, num_parts,
+                                               reinterpret_cast<float*>(checksums), nullptr, nullptr, nullptr,
+                                               nullptr);
+}
+
 // Combines the partitions of each (sequence, query head):
 // out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), M = max_p m_p.
 // The (m, l) of all partitions are staged in LDS once; each thread then sums
@@ -340,6 +361,80 @@ extern "C" int pa_decode_append(const pa_kv_pool* pool, int32_t layer, void* out
   return pa::decode_entry("pa_decode_append", pool, layer, out, q, B, H_q, block_tables, max_blocks, context_lens,
                           max_ctx, scale, workspace, workspace_bytes, pa::NewTokens{k_new, v_new, slot_mapping},
                           stream);
+}
+
+// ------------------------------------------------------ gather ceiling
+namespace pa {
+using GatherFn = void (*)(const pa_kv_pool*, int32_t, int32_t, const int32_t*, int32_t, const int32_t*, int32_t,
+                          const DecodePlan&, uint32_t*, hipStream_t);
+
+template <typename E, int D, int G, int BS>
+static void launch_gather(const pa_kv_pool* pool, int32_t layer, int32_t B, const int32_t* bt, int32_t max_blocks,
+                          const int32_t* ctx, int32_t H_q, const DecodePlan& pl, uint32_t* cs, hipStream_t stream) {
+  const int64_t head_stride = static_cast<int64_t>(pool->num_blocks) * BS * D * E::bytes;
+  const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * head_stride;
+  const size_t lds = static_cast<size_t>(pl.waves) * G * (D + 2) * sizeof(float);
+  dim3 grid(pool->num_kv_heads, pl.num_parts, B);
+  hipLaunchKernelGGL((gather_kernel<E, D, G, BS, max_threads<G>()>), grid, dim3(64 * pl.waves), lds, stream,
+                     static_cast<char*>(pool->k), static_cast<char*>(pool->v), layer_off, head_stride, bt, max_blocks,
+                     ctx, H_q, pl.blocks_per_part, pl.num_parts, pl.waves, cs);
+}
+template <typename E, int D, int G>
+static GatherFn gather_bs(int bs) {
+  switch (bs) {
+    case 8: return &launch_gather<E, D, G, 8>;
+    case 16: return &launch_gather<E, D, G, 16>;
+    case 32: return &launch_gather<E, D, G, 32>;
+  }
+  return nullptr;
+}
+template <typename E, int D>
+static GatherFn gather_g(int G, int bs) {
+  switch (G) {
+    case 1: return gather_bs<E, D, 1>(bs);
+    case 2: return gather_bs<E, D, 2>(bs);
+    case 4: return gather_bs<E, D, 4>(bs);
+    case 8: return gather_bs<E, D, 8>(bs);
+  }
+  return nullptr;
+}
+static size_t gather_bytes(const DecodePlan& pl, int B, int H_kv) {
+  return static_cast<size_t>(B) * pl.num_parts * H_kv * pl.waves * sizeof(uint32_t);
+}
+}  // namespace pa
+
+extern "C" size_t pa_gather_checksum_size(const pa_kv_pool* pool, int32_t B, int32_t H_q, int32_t max_ctx) {
+  using namespace pa;
+  if (!pool || B <= 0 || H_q <= 0 || pool->num_kv_heads <= 0 || pool->block_size <= 0 || H_q % pool->num_kv_heads)
+    return 0;
+  const DecodePlan pl = plan_decode(B, pool->num_kv_heads, H_q / pool->num_kv_heads, pool->block_size, max_ctx);
+  return gather_bytes(pl, B, pool->num_kv_heads);
+}
+
+extern "C" int pa_gather_checksum(const pa_kv_pool* pool, int32_t layer, int32_t B, int32_t H_q,
+                                  const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                                  int32_t max_ctx, uint32_t* checksums, size_t checksum_bytes, hipStream_t stream) {
+  using namespace pa;
+  const std::string w("pa_gather_checksum");
+  // validate_decode wants out and q; the walk reads neither
+  if (int e = validate_decode(w, pool, layer, checksums, pool ? pool->k : nullptr, B, H_q, block_tables, max_blocks,
+                              context_lens, max_ctx))
+    return e;
+  if (B == 0) return PA_OK;
+  const int G = H_q / pool->num_kv_heads;
+  GatherFn fn = nullptr;
+  if (pool->dtype == PA_BF16 && pool->head_dim == 128) fn = gather_g<BF16, 128>(G, pool->block_size);
+  if (pool->dtype == PA_BF16 && pool->head_dim == 64) fn = gather_g<BF16, 64>(G, pool->block_size);
+  if (!fn) return fail(PA_ENOTSUP, w + ": bf16 pools only");
+  const DecodePlan pl = plan_decode(B, pool->num_kv_heads, G, pool->block_size, max_ctx);
+  if (pl.num_parts > 65535) return fail(PA_EINVAL, w + ": too many partitions for the grid");
+  if (checksum_bytes < gather_bytes(pl, B, pool->num_kv_heads) || (reinterpret_cast<uintptr_t>(checksums) & 3u))
+    return fail(PA_ESPACE, w + ": checksum buffer too small or misaligned");
+  if (validate_on())
+    if (int e = check_decode_indices(w, pool, B, block_tables, max_blocks, context_lens, max_ctx, nullptr, stream))
+      return e;
+  fn(pool, layer, B, block_tables, max_blocks, context_lens, H_q, pl, checksums, stream);
+  return check_launch("pa_gather_checksum");
 }
 
 // ------------------------------------------------------ allocation-free decode

@@ -180,7 +180,13 @@ __device__ __forceinline__ void gather_heads(const uint32_t* own, uint32_t* all)
 // blocks_per_part, and the workgroup always writes (m, l, acc) partials,
 // which a merge combines with the prefix's; an empty partition writes
 // nothing.
-template <typename E, int D, int G, int BS, bool FUSED, bool SUFFIX = false>
+//
+// CHECKSUM: a measuring variant, not a decode: the same grid, block tables,
+// unit walk and K/V loads, but each unit's bytes are XORed into a checksum
+// instead of attended to (no q, no softmax, no output).  Each wave writes
+// its checksum (uint32) to ws_ml at ((b * num_parts + part) * H_kv + g) * W
+// + wave.  It measures what the decode's access pattern alone can stream.
+template <typename E, int D, int G, int BS, bool FUSED, bool SUFFIX = false, bool CHECKSUM = false>
 __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, int b, float* __restrict__ smem,
                                             char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off,
                                             int64_t head_stride, const char* __restrict__ q, void* __restrict__ out,
@@ -191,6 +197,7 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
                                             const char* __restrict__ v_new, const int32_t* __restrict__ new_slots,
                                             int skip_blocks = 0) {
   static_assert(!(SUFFIX && FUSED), "a shared-prefix decode appends beforehand");
+  static_assert(!(CHECKSUM && (FUSED || SUFFIX)), "the checksum walk is the plain decode's");
   using Sh = DecodeShape<E, D, BS, G>;
   constexpr int S = Sh::S, VEC = Sh::VEC, LPT = Sh::LPT, TPW = Sh::TPW, NLD = Sh::NLD, U = Sh::U, UPB = Sh::UPB,
                 RING = Sh::RING;
@@ -236,7 +243,10 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
     // Nothing visible in this partition.  With a single partition that means
     // an empty sequence: its rows are zeros.  Split partitions past the end
     // are not counted by the merge.
-    if (!SUFFIX && num_parts == 1) {
+    if constexpr (CHECKSUM) {
+      if (lane == 0)
+        reinterpret_cast<uint32_t*>(ws_ml)[((static_cast<int64_t>(b) * num_parts + part) * H_kv + g) * W + wave] = 0;
+    } else if (!SUFFIX && num_parts == 1) {
       for (int i = threadIdx.x; i < G * D; i += W * 64) store_elem(E{}, out, head0 * D + i, 0.0f);
     }
     return;
@@ -266,8 +276,10 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
   }
 
   QChunk<E> qc[G];
+  if constexpr (!CHECKSUM) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) qc[h].set(load16(q + ((head0 + h) * D + c * VEC) * S));
+    for (int h = 0; h < G; ++h) qc[h].set(load16(q + ((head0 + h) * D + c * VEC) * S));
+  }
 
   float m[NS], l[NS], acc[G][VEC];
 #pragma unroll
@@ -295,9 +307,16 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
     }
   };
 
+  uint32_t cs = 0;  // CHECKSUM: XOR of every loaded dword
+
   // One unit: NLD tokens per lane row, online-softmax update for G heads;
   // with ``masked``, tokens at positions >= vis_ take no part.
   auto process = [&](int u, const uint4* kr, const uint4* vr, bool masked, int vis_) {
+    if constexpr (CHECKSUM) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) cs ^= kr[i].x ^ kr[i].y ^ kr[i].z ^ kr[i].w ^ vr[i].x ^ vr[i].y ^ vr[i].z ^ vr[i].w;
+      return;
+    }
     const int tok0 = u * U + r;
     if constexpr (kScatter) {
       constexpr int NH = NS;
@@ -520,6 +539,14 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
     add_new_token();
   }
   if (has_tail) process(u_full, kt, vt, true, vis);
+
+  if constexpr (CHECKSUM) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cs ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(cs), off));
+    if (lane == 0)
+      reinterpret_cast<uint32_t*>(ws_ml)[((static_cast<int64_t>(b) * num_parts + part) * H_kv + g) * W + wave] = cs;
+    return;
+  }
 
   // Softmax state of all G heads in every lane: mg, lg.
   float mg[G], lg[G];
