@@ -18,8 +18,12 @@
 //    S = Q K^T and O = P V over them are dense contractions.  They run on
 //    the matrix cores through the prefill tile (no causal mask, all rows see
 //    every shared key), cut into key splits that write (m, l, o) partials.
-//  * suffix pass: every row's remaining blocks through the decode body,
-//    which writes (m, l, acc) partials per partition.
+//    A group whose rows times query heads fit one 32-row MFMA tile (a few
+//    samples or beams of one prompt) takes a streaming 32-row tile instead,
+//    which also reads each row's own keys past the shared blocks (its
+//    suffix) as further steps, masked to that row.
+//  * suffix pass: the remaining blocks of every other row through the
+//    decode body, which writes (m, l, acc) partials per partition.
 //  * both passes are one launch, prefix workgroups first; a merge launch
 //    combines each row's prefix and suffix partials into its output.
 #include <hip/hip_runtime.h>
@@ -36,14 +40,19 @@ namespace pa {
 
 constexpr int kMaxGroups = 64;
 
-// The groups of a launch (those with shared blocks), in the kernel arguments.
+// The groups of a launch (those with shared blocks), in the kernel
+// arguments, in the order of their first rows.
 struct GroupList {
   int32_t n;
   int32_t first_row[kMaxGroups];
   int32_t n_rows[kMaxGroups];
   int32_t shared_blocks[kMaxGroups];
   int32_t splits[kMaxGroups];          // key splits of the group's prefix
-  int32_t steps_per_split[kMaxGroups];  // 64-key steps per split
+  int32_t steps_per_split[kMaxGroups];  // key steps per split (64 or 32 keys)
+  // 32-row tile: 32-key steps per row of the rows' own keys past the shared
+  // blocks, streamed by the tile after the shared ones; -1: those keys go
+  // through the suffix pass.
+  int32_t tile_suffix[kMaxGroups];
   int32_t pre_before[kMaxGroups + 1];  // prefix workgroups before group c
   int64_t row_off[kMaxGroups];         // first partial row of group c ([split][row][head] rows)
 };
@@ -98,6 +107,367 @@ __global__ void __launch_bounds__(kPrefillThreads)
                                         nullptr, nullptr, nullptr, skip);
 }
 
+// ----------------------------------------------------- the 32-row prefix tile
+// A group whose rows times query heads fit one 32-row MFMA tile (the usual
+// case: a few samples or beams of one prompt) reads its shared keys with a
+// tile built for streaming rather than for the matrix cores: the pass is
+// bound by HBM (each K/V byte feeds only the group's 32 rows), so what
+// matters is how many loads are in flight.  A workgroup of 4 waves takes one
+// (group, KV head, key split); the waves take every 4th 32-key step of the
+// split, each with its next step's K and V in flight in a ring of its own in
+// LDS, with no barrier between steps.  Every global load goes straight into
+// LDS (global_load_lds_dwordx4) and is waited for by explicit counts, so
+// that the compiler's own load tracking never makes a step wait for the
+// step behind it.  K and V tiles use the prefill tile's LDS layout, so the
+// MFMA operand reads and the transposing V reads are the ones it uses.  At
+// the end the 4 waves merge their (m, l, O) through LDS into one partial.
+constexpr int kShWaves = 4;
+constexpr int kShThreads = 64 * kShWaves;
+constexpr int kShKT = 32;     // keys per step
+constexpr int kShStages = 2;  // steps in flight per wave
+
+template <int D>
+struct ShLayout {
+  static constexpr int ROWB = D * 2;                 // bytes of a K/V/q row
+  static constexpr int TILE = kShKT * ROWB;          // one 32-row tile
+  static constexpr int COLS = ROWB / 64;             // 64-byte columns
+  static constexpr int LOADS = TILE / 1024;          // 1 KiB direct loads per tile
+  static constexpr int STAGE = 2 * TILE;             // K then V
+  static constexpr int RING = kShStages * STAGE;     // one wave's ring
+  static constexpr int QOFF = kShWaves * RING;       // the 32 query rows
+  static constexpr int BYTES = QOFF + TILE;
+  static_assert(LOADS == 2 * COLS, "two 16-row groups per tile");
+  static_assert(32 * D * 4 + 2 * 32 * 4 <= RING, "a wave's (o, m, l) fit its ring");
+};
+
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt at their maxima (gfx9 encoding).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Steps of a group: P = ceil(S / 32) steps over the shared keys [0, S),
+// all rows' (table: the group's first row), then, with U >= 0, U steps per
+// row over its own keys [S, S + 32 U) (table: that row's; keys at or past
+// its length are masked, and rows of the other samples see none of them).
+// The tile takes steps [v_lo, v_hi).
+template <typename E, int D, int G, int BS>
+__device__ __forceinline__ void prefix_tile32(int g, int n_rows, int v_lo, int v_hi, int S, int U,
+                                              char* __restrict__ lds, const char* __restrict__ pool_k,
+                                              const char* __restrict__ pool_v, int64_t layer_off, int64_t head_stride,
+                                              const char* __restrict__ q, const int32_t* __restrict__ table,
+                                              int32_t max_blocks, const int32_t* __restrict__ lens, int32_t H_q,
+                                              float scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  using M = Mfma<E>;
+  using vec = typename M::vec;
+  using L = ShLayout<D>;
+  constexpr int KT = kShKT;
+  constexpr int KS = D / 16;  // QK k-steps over the head dim
+  constexpr int DT = D / 32;  // 32-dim output tiles
+  constexpr int LPS = 2 * L::LOADS;  // direct loads per step (K and V)
+  static_assert(BS >= 8, "at most two blocks per 16-row group");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 31;
+  const int h = lane >> 5;
+  const int rows = n_rows * G;  // live query rows: (sample r / G, head g * G + r % G)
+
+  const char* kbase = pool_k + layer_off + static_cast<int64_t>(g) * head_stride;
+  const char* vbase = pool_v + layer_off + static_cast<int64_t>(g) * head_stride;
+  char* ring = lds + wave * L::RING;
+  char* qt = lds + L::QOFF;
+
+  // Direct loads: load i of a tile fills 16 rows (group rg = i / COLS) of
+  // one 64-byte column (i % COLS); lane l lands at byte 16 l: row 16 rg +
+  // l / 4, rotated chunk position l % 4 (the prefill tile's layout).
+  const int lrow = lane >> 2;
+  auto chunk_of = [&](int row) { return ((lane & 3) ^ ((row >> 2) & 3)) * 16; };
+
+  // The 32 query rows, loaded once per workgroup: wave w issues loads
+  // w, w + 4, ... of the q tile.  Rows past the group's are clamped (never
+  // stored).
+#pragma unroll
+  for (int i = wave; i < L::LOADS; i += kShWaves) {
+    const int rg = i / L::COLS, col = i % L::COLS;
+    const int r = min(rg * 16 + lrow, rows - 1);
+    const char* src = q + ((static_cast<int64_t>(r / G) * H_q + g * G + r % G) * D) * 2 + col * 64 +
+                      chunk_of(rg * 16 + lrow);
+    load_to_lds(src, qt + col * (KT * 64) + rg * 1024);
+  }
+
+  // Steps of this wave: steps v_lo + wave, v_lo + wave + 4, ... (an index
+  // past the wave's last is clamped to it: its loads repeat, unused).
+  const int nsteps = v_hi - v_lo;
+  const int nw = nsteps > wave ? (nsteps - wave + kShWaves - 1) / kShWaves : 0;
+  const int P = (S + KT - 1) / KT;
+  const int Us = max(U, 1);
+  auto v_of = [&](int j) { return v_lo + wave + min(j, nw - 1) * kShWaves; };
+  // A step's first key and key limit, and its table row (-1: the shared
+  // keys) -- all wave-uniform.
+  auto row_of = [&](int v) { return v < P ? -1 : (v - P) / Us; };
+  auto key0_of = [&](int v) { return v < P ? v * KT : S + (v - P) % Us * KT; };
+  const int32_t spare = table[0];  // a block of the group: loads past a row's end read it, unused
+  struct Step {
+    int32_t b[2][2];  // [row group][rows 0-7 / 8-15]
+    int32_t k0, lim;  // first key; keys at or past lim are not the step's
+  };
+  // The step's table entries and the row's length (scalar loads, waited
+  // for with the LDS reads of a later step).  Entries are read at their
+  // index clamped to the table; one past the row's length is never used.
+  auto fetch = [&](int j) __attribute__((always_inline)) {
+    Step st;
+    const int v = v_of(j);
+    const int row = row_of(v);
+    st.k0 = key0_of(v);
+    st.lim = row < 0 ? S : lens[row];
+    const int32_t* tab = table + static_cast<int64_t>(max(row, 0)) * max_blocks;
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      st.b[rg][0] = tab[min((st.k0 + rg * 16) / BS, max_blocks - 1)];
+      st.b[rg][1] = BS >= 16 ? st.b[rg][0] : tab[min((st.k0 + rg * 16 + 8) / BS, max_blocks - 1)];
+    }
+    return st;
+  };
+  auto issue = [&](const Step& st, int slot) __attribute__((always_inline)) {
+    char* kt = ring + slot * L::STAGE;
+    char* vt = kt + L::TILE;
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      // A lane's 8 or 16 rows sit in one block (S is a multiple of the
+      // block size, steps start 32 keys apart): past the limit, the spare.
+      const int first = st.k0 + rg * 16 + ((BS >= 16 || lrow < 8) ? 0 : 8);
+      const bool past = first >= st.lim;
+      const int key = past ? 0 : min(st.k0 + rg * 16 + lrow, st.lim - 1);
+      const int64_t blk = past ? spare : ((BS >= 16 || lrow < 8) ? st.b[rg][0] : st.b[rg][1]);
+      const int64_t off = (blk * BS + (key & (BS - 1))) * L::ROWB + chunk_of(rg * 16 + lrow);
+#pragma unroll
+      for (int col = 0; col < L::COLS; ++col) {
+        load_to_lds(kbase + off + col * 64, kt + col * (KT * 64) + rg * 1024);
+        load_to_lds(vbase + off + col * 64, vt + col * (KT * 64) + rg * 1024);
+      }
+    }
+  };
+
+  // The key limit the next step computed needs, loaded a step ahead.  Every
+  // value loaded here is used once, in the next iteration, and reloaded
+  // only after that use: a value carried further would make the loop wait
+  // for the scalar loads it has just issued.
+  auto lim_of = [&](int j) __attribute__((always_inline)) {
+    const int row = row_of(v_of(j));
+    return row < 0 ? S : lens[row];
+  };
+  Step next{};
+  int limc = 0;
+  if (nw > 0) {
+    issue(fetch(0), 0);
+    issue(fetch(1), 1);
+    next = fetch(2);
+    limc = lim_of(0);
+  }
+  // q landed (each wave waits for its own q loads; the steps behind them may
+  // stay in flight), then the workgroup's q loads are all visible.
+  if (nw > 0) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPS));
+  } else {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  }
+  barrier_keep_loads();
+
+  vec qb[KS];
+  const int kb_even = tile_off<KT>(li, h), kb_odd = tile_off<KT>(li, 2 + h);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qb[ks] = *reinterpret_cast<const vec*>(qt + (ks >> 1) * (KT * 64) + ((ks & 1) ? kb_odd : kb_even));
+  // transposing V reads: as the prefill tile's, for one 32-key tile
+  const int g16 = lane >> 4, k4 = (lane >> 2) & 3, q4 = lane & 3;
+  const int vrow = 4 * (g16 >> 1) + k4, vch = (g16 & 1) * 2 + (q4 >> 1);
+  const int vb_lo = tile_off<KT>(vrow, vch) + (q4 & 1) * 8, vb_hi = tile_off<KT>(vrow + 8, vch) + (q4 & 1) * 8;
+
+  float m = -INFINITY, lsum = 0.0f;
+  floatx16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = floatx16_t{};
+  const float c = scale_log2 > 0.0f ? scale_log2 : 1.0f;
+
+  for (int j = 0; j < nw; ++j) {
+    const int slot = j & 1;
+    const char* kt = ring + slot * L::STAGE;
+    const char* vt = kt + L::TILE;
+    // step j has landed; step j + 1 (LPS loads) may still be in flight
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS));
+    vec ka[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ka[ks] = *reinterpret_cast<const vec*>(kt + (ks >> 1) * (KT * 64) + ((ks & 1) ? kb_odd : kb_even));
+    vec va[2][DT];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const char* vs = vt + (s2 * 16) * 64 + dt * (KT * 64);
+        const uint2 lo = lds_read_tr(vs + vb_lo);
+        const uint2 hi = lds_read_tr(vs + vb_hi);
+        va[s2][dt] = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      }
+    // Every read of this slot is back before its refill (step j + 2) lands
+    // in it; the refill index is clamped, so every wave issues the same
+    // number of loads per step and the counts above stay exact.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    issue(next, slot);
+    next = fetch(j + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    const int lim = limc;
+    const int vj = v_of(j);
+    const int key0 = key0_of(vj);
+    if (key0 < lim) {  // uniform: not a step wholly past its row's length
+      floatx16_t st = floatx16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) st = M::mma(ka[ks], qb[ks], st);
+      // online softmax of this step's 32 keys (lane: 16 keys of row li, the
+      // other 16 in lane li + 32): log2 domain, scale folded into the exponent
+      if (scale_log2 <= 0.0f) st *= scale_log2;
+      const int row = row_of(vj);
+      if (row >= 0 || key0 + KT > lim) {  // uniform: a row's own keys, or a partial step
+        const bool mine = row < 0 || li / G == row;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (!mine || key0 + 8 * (i >> 2) + 4 * h + (i & 3) >= lim) st[i] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[v]);
+      mx = max_halves(mx);
+      const float mcand = mx * c;
+      if (__any(mcand > m + kSlack)) {
+        const float mnew = fmaxf(m, mcand);
+        const float alpha = __builtin_amdgcn_exp2f(m - ((mnew == -INFINITY) ? 0.0f : mnew));
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      }
+      const float ms = (m == -INFINITY) ? 0.0f : m;
+      vec pb[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        uint16_t hh[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(st[8 * s2 + i], c, -ms));
+          lsum += p;
+          hh[i] = M::cvt(p);
+        }
+        pb[s2] = __builtin_bit_cast(vec, make_uint4(hh[0] | (uint32_t(hh[1]) << 16), hh[2] | (uint32_t(hh[3]) << 16),
+                                                    hh[4] | (uint32_t(hh[5]) << 16), hh[6] | (uint32_t(hh[7]) << 16)));
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = M::mma(va[s2][dt], pb[s2], o[dt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    limc = lim_of(j + 1);
+  }
+
+  // Merge the 4 waves through LDS (each wave's ring, once its own loads
+  // have all landed): o as [32 rows][D] fp32, then m and l per row.
+  const float lt = sum_halves(lsum);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  float* wo = reinterpret_cast<float*>(ring);
+  float* wm = wo + 32 * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      *reinterpret_cast<float4*>(wo + li * D + dt * 32 + 8 * jj + 4 * h) =
+          make_float4(o[dt][4 * jj], o[dt][4 * jj + 1], o[dt][4 * jj + 2], o[dt][4 * jj + 3]);
+  if (h == 0) {
+    wm[li] = m;
+    wm[32 + li] = lt;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rows * D; idx += kShThreads) {
+    const int r = idx / D, e = idx % D;
+    float mw[kShWaves], mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kShWaves; ++w) {
+      mw[w] = reinterpret_cast<const float*>(lds + w * L::RING)[32 * D + r];
+      mx = fmaxf(mx, mw[w]);
+    }
+    const float msafe = (mx == -INFINITY) ? 0.0f : mx;
+    float acc = 0.0f, lw = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kShWaves; ++w) {
+      const float* base = reinterpret_cast<const float*>(lds + w * L::RING);
+      const float wt = __builtin_amdgcn_exp2f(mw[w] - msafe);
+      acc += base[r * D + e] * wt;
+      lw += base[32 * D + 32 + r] * wt;
+    }
+    const int64_t row = static_cast<int64_t>(r / G) * H_q + g * G + r % G;
+    ws_o[row * D + e] = acc;
+    if (e == 0) *reinterpret_cast<float2*>(ws_ml + 2 * row) = make_float2(mx, lw);
+  }
+}
+
+// Prefix tiles of 32 rows (groups whose rows times query heads fit one MFMA
+// tile) and the suffix decode, 4 waves per workgroup.  Workgroup i takes
+// prefix item i (group, KV head, split) if there is one, then the suffix
+// items i, i + grid, i + 2 grid, ... in the decode kernel's order over the
+// rows whose suffix the tile does not stream: a workgroup's LDS takes most
+// of a CU, so a suffix item of a few blocks launched as a workgroup of its
+// own would hold a CU for a whole dispatch.
+template <typename E, int D, int G, int BS>
+__global__ void __launch_bounds__(kShThreads)
+    shared_decode32_kernel(char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off,
+                           int64_t head_stride, int32_t H_kv, int32_t H_q, float scale_log2, const char* __restrict__ q,
+                           const int32_t* __restrict__ block_tables, int32_t max_blocks,
+                           const int32_t* __restrict__ context_lens, int32_t blocks_per_part, int32_t num_parts,
+                           float* __restrict__ ws_ml, float* __restrict__ ws_acc, float* __restrict__ pre_o,
+                           float* __restrict__ pre_ml, int32_t n_pre, int32_t n_dec, GroupList gl) {
+  static_assert(kShWaves * G * (D + 2) * sizeof(float) <= ShLayout<D>::BYTES, "decode merge fits the LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[ShLayout<D>::BYTES];
+  const int id = blockIdx.x;
+  if (id < n_pre) {
+    int c = 0;
+    while (id >= gl.pre_before[c + 1]) ++c;
+    const int local = id - gl.pre_before[c];
+    const int g = local % H_kv;  // KV head fastest: the heads of one split spread over the XCDs
+    const int split = local / H_kv;
+    const int n = gl.n_rows[c];
+    const int S = gl.shared_blocks[c] * BS;
+    const int U = gl.tile_suffix[c];
+    const int steps = (S + kShKT - 1) / kShKT + (U > 0 ? n * U : 0);
+    const int v_lo = split * gl.steps_per_split[c];
+    const int v_hi = min(steps, v_lo + gl.steps_per_split[c]);
+    const int64_t roff = gl.row_off[c] + static_cast<int64_t>(split) * n * H_q;
+    prefix_tile32<E, D, G, BS>(g, n, v_lo, v_hi, S, U, lds, pool_k, pool_v, layer_off, head_stride,
+                               q + static_cast<int64_t>(gl.first_row[c]) * H_q * D * 2,
+                               block_tables + static_cast<int64_t>(gl.first_row[c]) * max_blocks, max_blocks,
+                               context_lens + gl.first_row[c], H_q, scale_log2, pre_o + roff * D, pre_ml + roff * 2);
+  }
+  for (int j = id; j < n_dec; j += gridDim.x) {
+    __syncthreads();  // the previous tile's or item's last LDS reads are done
+    const int g = j % H_kv;
+    const int rest = j / H_kv;
+    // the (rest / num_parts)-th row outside the groups whose suffix the
+    // tile streams (groups in row order)
+    int b = rest / num_parts;
+    for (int c = 0; c < gl.n; ++c)
+      if (gl.tile_suffix[c] >= 0 && b >= gl.first_row[c]) b += gl.n_rows[c];
+    int part = rest % num_parts;
+    if (num_parts >= 4) {
+      part += b & 3;
+      if (part >= num_parts) part -= num_parts;
+    }
+    int skip = 0;
+    for (int c = 0; c < gl.n; ++c)
+      if (b >= gl.first_row[c] && b < gl.first_row[c] + gl.n_rows[c]) skip = gl.shared_blocks[c];
+    decode_body<E, D, G, BS, false, true>(kShWaves, g, part, H_kv, b, reinterpret_cast<float*>(lds), pool_k, pool_v,
+                                          layer_off, head_stride, q, nullptr, block_tables, max_blocks, context_lens,
+                                          scale_log2, H_q, blocks_per_part, num_parts, ws_ml, ws_acc, nullptr,
+                                          nullptr, nullptr, skip);
+  }
+}
+
 // Combines each (sequence, query head)'s partials: the prefix splits of its
 // group (if any) and the suffix partitions that hold some of its blocks:
 // out = sum_k o_k 2^(m_k - M) / sum_k l_k 2^(m_k - M), M = max_k m_k.  Every
@@ -121,8 +491,10 @@ __global__ void __launch_bounds__(D)
     if (b >= gl.first_row[k] && b < gl.first_row[k] + gl.n_rows[k]) c = k;
   const int skip = c >= 0 ? gl.shared_blocks[c] : 0;
   const int ns = c >= 0 ? gl.splits[c] : 0;
-  const int nblk = (context_lens[b] + bs - 1) / bs;
-  const int np = max(0, min(num_parts, (nblk - skip + blocks_per_part - 1) / blocks_per_part));
+  // a row whose suffix the 32-row tile streamed has its splits only
+  const bool streamed = c >= 0 && gl.tile_suffix[c] >= 0;
+  const int nblk = streamed ? 0 : (context_lens[b] + bs - 1) / bs;
+  const int np = streamed ? 0 : max(0, min(num_parts, (nblk - skip + blocks_per_part - 1) / blocks_per_part));
   const int nk = ns + np;
   // partial k: prefix split k (k < ns) or suffix partition k - ns
   const int64_t prow0 = c >= 0 ? gl.row_off[c] + static_cast<int64_t>(b - gl.first_row[c]) * H_q + hd : 0;
@@ -180,6 +552,8 @@ struct SharedPlan {
   int32_t n_pre;
   int64_t pre_rows;  // prefix partial rows (sum over groups of splits * n_rows * H_q)
   int32_t max_splits;
+  int32_t loose_rows;  // rows whose suffix goes through the suffix pass
+  bool tile32;         // every group fits one 32-row tile: the streaming prefix tile
 };
 
 // Host checks of a group list and the launch plan (PA_OK or an error).
@@ -204,44 +578,74 @@ static int plan_shared(const std::string& w, const pa_kv_pool* pool, int32_t B, 
   for (size_t i = 1; i < spans.size(); ++i)
     if (spans[i].first < spans[i - 1].second) return fail(PA_EINVAL, w + ": groups overlap");
 
+  // Groups of at most 32 query rows per KV head (rows times query heads)
+  // take the streaming 32-row tile; any larger group sends the whole launch
+  // through the prefill tile.
+  p->tile32 = pool->head_dim == 128 || pool->head_dim == 64;
+  for (int c = 0; c < n_groups; ++c)
+    if (groups[c].shared_blocks > 0 && static_cast<int64_t>(groups[c].n_rows) * G > 32) p->tile32 = false;
   p->dec = plan_decode(B, pool->num_kv_heads, G, bs, max_ctx);
-  p->dec.waves = kPrefillWaves;  // the fused kernel's workgroups are 8 waves
+  p->dec.waves = p->tile32 ? kShWaves : kPrefillWaves;  // the fused kernel's workgroup size
   if (p->dec.num_parts > 65535) return fail(PA_EINVAL, w + ": too many partitions for the grid");
-  // Key splits: about two workgroups per CU over all groups' prefix items,
-  // at least two 64-key steps each.
-  const int TP = kRowsPerWave * kPrefillWaves / G;
+  // Groups with shared blocks, in row order.  The 32-row tile also streams
+  // a group's own keys past the shared blocks, U = ceil((max_ctx - S) / 32)
+  // steps per row (a bound: a row's steps past its length are skipped), when
+  // those are at most as many as its shared steps; otherwise, and for the
+  // prefill tile, they go through the suffix pass.
+  std::vector<int> order;
+  for (int c = 0; c < n_groups; ++c)
+    if (groups[c].shared_blocks > 0) order.push_back(c);
+  std::sort(order.begin(), order.end(),
+            [&](int a, int b2) { return groups[a].first_row < groups[b2].first_row; });
+  const int KT = p->tile32 ? kShKT : kKeysPerStep;
+  const int TP = p->tile32 ? 32 / G : kRowsPerWave * kPrefillWaves / G;
+  std::vector<int64_t> steps(order.size());
+  std::vector<int32_t> tile_suffix(order.size(), -1);
   int64_t item_steps = 0;
-  for (int c = 0; c < n_groups; ++c) {
-    const int64_t steps = ceil_div(static_cast<int64_t>(groups[c].shared_blocks) * bs, kKeysPerStep);
-    item_steps += ceil_div(groups[c].n_rows, TP) * pool->num_kv_heads * steps;
+  int64_t loose = B;
+  for (size_t k = 0; k < order.size(); ++k) {
+    const pa_share_group& gr = groups[order[k]];
+    const int64_t S = static_cast<int64_t>(gr.shared_blocks) * bs;
+    steps[k] = ceil_div(S, KT);
+    const int64_t U = ceil_div(std::max<int64_t>(0, max_ctx - S), kShKT);
+    if (p->tile32 && gr.n_rows * U <= steps[k]) {
+      tile_suffix[k] = static_cast<int32_t>(U);
+      steps[k] += gr.n_rows * U;
+      loose -= gr.n_rows;
+    }
+    item_steps += ceil_div(gr.n_rows, TP) * pool->num_kv_heads * steps[k];
   }
-  const int64_t target = 2 * static_cast<int64_t>(device_cus());
-  const int sps = static_cast<int>(std::max<int64_t>(2, ceil_div(item_steps, target)));
+  // Key splits.  Prefill tile: about two workgroups per CU, at least two
+  // 64-key steps each.  32-row tile: about one workgroup per CU (its LDS
+  // holds one), at least one 32-key step per wave.
+  const int64_t target = (p->tile32 ? 1 : 2) * static_cast<int64_t>(device_cus());
+  const int sps = static_cast<int>(std::max<int64_t>(p->tile32 ? kShWaves : 2, ceil_div(item_steps, target)));
   GroupList& gl = p->gl;
   gl = GroupList{};
   gl.pre_before[0] = 0;
   int64_t pre = 0, rows = 0;
   int max_splits = 0;
-  for (int c = 0; c < n_groups; ++c) {
-    if (groups[c].shared_blocks == 0) continue;
-    const int k = gl.n++;
-    const int64_t steps = ceil_div(static_cast<int64_t>(groups[c].shared_blocks) * bs, kKeysPerStep);
-    gl.first_row[k] = groups[c].first_row;
-    gl.n_rows[k] = groups[c].n_rows;
-    gl.shared_blocks[k] = groups[c].shared_blocks;
+  for (size_t k = 0; k < order.size(); ++k) {
+    const pa_share_group& gr = groups[order[k]];
+    gl.n = static_cast<int32_t>(k + 1);
+    gl.first_row[k] = gr.first_row;
+    gl.n_rows[k] = gr.n_rows;
+    gl.shared_blocks[k] = gr.shared_blocks;
     gl.steps_per_split[k] = sps;
-    gl.splits[k] = static_cast<int32_t>(ceil_div(steps, sps));
+    gl.tile_suffix[k] = tile_suffix[k];
+    gl.splits[k] = static_cast<int32_t>(ceil_div(steps[k], sps));
     gl.row_off[k] = rows;
-    rows += static_cast<int64_t>(gl.splits[k]) * groups[c].n_rows * H_q;
-    pre += ceil_div(groups[c].n_rows, TP) * pool->num_kv_heads * gl.splits[k];
+    rows += static_cast<int64_t>(gl.splits[k]) * gr.n_rows * H_q;
+    pre += ceil_div(gr.n_rows, TP) * pool->num_kv_heads * gl.splits[k];
     gl.pre_before[k + 1] = static_cast<int32_t>(std::min<int64_t>(pre, INT32_MAX));
     max_splits = std::max(max_splits, gl.splits[k]);
   }
-  const int64_t n_dec = static_cast<int64_t>(pool->num_kv_heads) * p->dec.num_parts * B;
+  const int64_t n_dec = static_cast<int64_t>(pool->num_kv_heads) * p->dec.num_parts * loose;
   if (pre + n_dec > INT32_MAX) return fail(PA_EINVAL, w + ": grid too large");
   p->n_pre = static_cast<int32_t>(pre);
   p->pre_rows = rows;
   p->max_splits = max_splits;
+  p->loose_rows = static_cast<int32_t>(loose);
   return PA_OK;
 }
 
@@ -267,12 +671,24 @@ static void launch_shared(const pa_kv_pool* pool, int32_t layer, void* out, cons
   float* pre_ml = pre_o + p.pre_rows * D;
   float* ws_acc = pre_ml + p.pre_rows * 2;
   float* ws_ml = ws_acc + dec_rows * D;
-  const int64_t n_dec = static_cast<int64_t>(pool->num_kv_heads) * p.dec.num_parts * B;
-  hipLaunchKernelGGL((shared_decode_kernel<E, D, G, BS>), dim3(static_cast<uint32_t>(p.n_pre + n_dec)),
-                     dim3(kPrefillThreads), 0, stream, static_cast<char*>(pool->k), static_cast<char*>(pool->v),
-                     layer_off, head_stride, pool->num_kv_heads, H_q, scale_log2, static_cast<const char*>(q), bt,
-                     max_blocks, ctx, p.dec.blocks_per_part, p.dec.num_parts, ws_ml, ws_acc, pre_o, pre_ml, p.n_pre,
-                     p.gl);
+  const int64_t n_dec = static_cast<int64_t>(pool->num_kv_heads) * p.dec.num_parts * p.loose_rows;
+  if (p.tile32) {
+    // One workgroup per prefix item, at least one per CU while suffix items
+    // remain; the suffix items are spread over them.
+    const int64_t grid = std::max<int64_t>(p.n_pre, std::min<int64_t>(n_dec, device_cus()));
+    if (grid > 0)
+      hipLaunchKernelGGL((shared_decode32_kernel<E, D, G, BS>), dim3(static_cast<uint32_t>(grid)), dim3(kShThreads),
+                         0, stream, static_cast<char*>(pool->k), static_cast<char*>(pool->v), layer_off, head_stride,
+                         pool->num_kv_heads, H_q, scale_log2, static_cast<const char*>(q), bt, max_blocks, ctx,
+                         p.dec.blocks_per_part, p.dec.num_parts, ws_ml, ws_acc, pre_o, pre_ml, p.n_pre,
+                         static_cast<int32_t>(n_dec), p.gl);
+  } else {
+    hipLaunchKernelGGL((shared_decode_kernel<E, D, G, BS>), dim3(static_cast<uint32_t>(p.n_pre + n_dec)),
+                       dim3(kPrefillThreads), 0, stream, static_cast<char*>(pool->k), static_cast<char*>(pool->v),
+                       layer_off, head_stride, pool->num_kv_heads, H_q, scale_log2, static_cast<const char*>(q), bt,
+                       max_blocks, ctx, p.dec.blocks_per_part, p.dec.num_parts, ws_ml, ws_acc, pre_o, pre_ml,
+                       p.n_pre, p.gl);
+  }
   const size_t lds = (p.max_splits + p.dec.num_parts) * sizeof(float);
   hipLaunchKernelGGL((shared_merge_kernel<E, D>), dim3(static_cast<uint32_t>(B) * H_q), dim3(D), lds, stream, out,
                      ws_ml, ws_acc, pre_o, pre_ml, ctx, H_q, p.dec.num_parts, p.dec.blocks_per_part, BS, p.gl);
