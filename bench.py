@@ -467,7 +467,7 @@ def main():
 
     # ---------------------------------------------------------- B=64: config 3
     scn3 = build_scenario(3, 0, bs=16)
-    g3 = DeviceRun(scn3, device=dev, num_layers=1, fill="randn")
+    g3 = DeviceRun(scn3, device=dev, num_layers=1, fill="randn", pad_pool=True)
     g3.run_setup()
     si3 = g3.prepare(scn3.steps[0], longest_first=True)
     # the same step launched in batch order: the launch rows permuted back
@@ -484,8 +484,9 @@ def main():
     b3 = decode_bytes(lens3, 40, 40, 128, 16, 2)
     out["attention_tok_s_b64"] = round(64 / (ms3 * 1e-3), 1)
     a3 = append_bytes(64, 40, 128, 2)
-    out["b64"] = {"workload": "13b-shaped MHA decode layer, B=64, 40 heads, block 16, lognormal ctx, churned pool; "
-                              "append + decode in one launch, batch submitted longest context first",
+    out["b64"] = {"workload": "13b-shaped MHA decode layer, B=64, 40 heads, block 16, lognormal ctx, churned pool "
+                              "(0x2080000 bytes per KV head); append + decode in one launch, batch submitted "
+                              "longest context first",
                   "ms_per_step": round(ms3, 5), "decode_ms": round(ms3d, 5),
                   "decode_GBps": round(b3 / (ms3d * 1e-3) / 1e9, 1),
                   "decode_hbm_frac": round(b3 / (ms3d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -500,7 +501,7 @@ def main():
                     "decode_GBps": round(b3 / (ms3d * 1e-3) / 1e9, 1)}}
     for bs in (8, 32):
         scn_bs = build_scenario(3, 0, bs=bs)
-        g_bs = DeviceRun(scn_bs, device=dev, num_layers=1, fill="randn")
+        g_bs = DeviceRun(scn_bs, device=dev, num_layers=1, fill="randn", pad_pool=True)
         g_bs.run_setup()
         si_bs = g_bs.prepare(scn_bs.steps[0], longest_first=True)
         ms_f = time_loop(torch, lambda i: g_bs.launch(si_bs, fused=True), n3, 5)
@@ -512,6 +513,16 @@ def main():
         del g_bs, si_bs
         torch.cuda.empty_cache()
     out["b64"]["block_size_sweep"] = {k: sweep[k] for k in ("8", "16", "32")}
+    out["b64"]["block_size_sweep"]["pool"] = ("each KV head's pool allocated at 0x2080000 bytes for every block size "
+                                              "(the block manager hands out 64 * (2048 / bs + 1) blocks)")
+    # the unpadded block-16 pool (8,256 blocks: a 0x2040000-byte head stride)
+    g_u = DeviceRun(scn3, device=dev, num_layers=1, fill="randn")
+    g_u.run_setup()
+    si_u = g_u.prepare(scn3.steps[0], longest_first=True)
+    out["b64"]["block16_unpadded_pool_decode_ms"] = round(
+        time_loop(torch, lambda i: g_u.launch(si_u, do_copy=False, do_append=False), n3, 5), 5)
+    del g_u, si_u
+    torch.cuda.empty_cache()
 
     # ---------------------------------------------------------- other rows
     if not args.no_rows:

@@ -45,6 +45,12 @@ CONFIGS = {
         d=128,
         bs=16,  # swept over 8 / 16 / 32
         num_blocks=None,  # 64 * (2048 // bs + 1): room for the longest context + 1
+        # Device allocation per KV head for timing runs (the block manager
+        # still hands out num_blocks): the same 0x2080000-byte stride at
+        # every block size.  The default pools' strides differ per block
+        # size, and 0x2040000 bytes (block 16's 8,256 blocks) alone slows
+        # a 40-head decode by 7-11% at any block size.
+        alloc_bytes_per_head=0x2080000,
         churn_rounds=256,
         kind="decode",
     ),

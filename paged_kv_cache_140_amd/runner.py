@@ -54,13 +54,20 @@ class DeviceRun:
     "randn" fills it with N(0,1) on the device and skips writing the history
     values (timing runs only need the bookkeeping), None leaves it as is."""
 
-    def __init__(self, scn, device="cuda", num_layers=1, layer=0, fill="nan", seed_fill=0):
+    def __init__(self, scn, device="cuda", num_layers=1, layer=0, fill="nan", seed_fill=0, pad_pool=False):
+        """``pad_pool``: allocate the workload's ``alloc_bytes_per_head`` per
+        KV head (if it names one) instead of exactly num_blocks blocks; the
+        block manager hands out num_blocks either way."""
         self.scn, self.cfg = scn, scn.cfg
         cfg = self.cfg
         self.device = device
         self.layer = layer
         self.bm = BlockManager(cfg["num_blocks"], cfg["bs"], gen.free_order(cfg, scn.seed))
-        self.pool = KVPool(num_layers, cfg["H_kv"], cfg["num_blocks"], cfg["bs"], cfg["d"], cfg["dtype"], device)
+        n_alloc = cfg["num_blocks"]
+        if pad_pool and cfg.get("alloc_bytes_per_head"):
+            per_block = cfg["bs"] * cfg["d"] * TORCH_DTYPE[cfg["dtype"]].itemsize
+            n_alloc = max(n_alloc, cfg["alloc_bytes_per_head"] // per_block)
+        self.pool = KVPool(num_layers, cfg["H_kv"], n_alloc, cfg["bs"], cfg["d"], cfg["dtype"], device)
         self.write_history = fill != "randn"
         if fill == "nan":
             self.pool.k.fill_(float("nan"))
