@@ -22,6 +22,7 @@ on the workloads that exercise them.
 
 import argparse
 import copy
+import dataclasses
 import json
 import os
 import sys
@@ -400,6 +401,29 @@ def main():
     def gather_contiguous(i):
         pa.pa_gather_checksum(gpu.pool, i % L, cfg["H_q"], contig_d, si.lens, si.max_ctx, cs_buf)
 
+    # Fixed cost per launch: the plain decode of the same batch and tables
+    # with every context cut to 1/2 and 1/4 of its length; the least-squares
+    # line through (bytes, ms) of the three gives the launch's fixed time
+    # (intercept) and its marginal streaming rate (1 / slope).
+    fit_bytes, fit_ms = [dbytes], [ms_decode]
+    for div in (2, 4):
+        l_f = np.maximum(lens // div, 1).astype(np.int32)
+        si_f = dataclasses.replace(si, lens=torch.from_numpy(l_f).to(dev), max_ctx=int(l_f.max()),
+                                   workspace=pa.decode_workspace(gpu.pool, len(l_f), cfg["H_q"], int(l_f.max())))
+
+        def decode_cut(i, si_f=si_f):
+            gpu.layer = i % L
+            gpu.launch(si_f, do_copy=False, do_append=False)
+
+        fit_ms.append(time_loop(torch, decode_cut, args.steps, args.warmup))
+        fit_bytes.append(decode_bytes(l_f, cfg["H_kv"], cfg["H_q"], cfg["d"], cfg["bs"], s))
+    slope, icept = np.polyfit(np.array(fit_bytes, dtype=np.float64), np.array(fit_ms), 1)
+    fixed_cost = {"what": "pa_decode of the same batch and tables with contexts cut to 1, 1/2 and 1/4 of their "
+                          "lengths; least-squares line through (bytes, ms)",
+                  "bytes": fit_bytes, "ms": [round(x, 5) for x in fit_ms],
+                  "fixed_us": round(icept * 1e3, 2), "marginal_GBps": round(1e-6 / slope, 1),
+                  "marginal_hbm_frac": round(1e-6 / slope / HBM_PEAK_GBS, 4)}
+
     gather_times = time_replays(torch, gather_scattered, args.steps, args.warmup, 11)
     ms_gather = gather_times[len(gather_times) // 2]
     ms_gather_c = time_loop(torch, gather_contiguous, args.steps, args.warmup)
@@ -453,6 +477,7 @@ def main():
         "decode_only_GBps": round(dbytes / (ms_decode * 1e-3) / 1e9, 1),
         "decode_bytes": dbytes,
         "decode_split_workspace_bytes": plan_ws,
+        "decode_fixed_cost": fixed_cost,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
