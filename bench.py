@@ -54,7 +54,7 @@ COUNTED = {
     "decode_b64_mha40_bs8": ("pa::decode_kernel<pa::BF16, 128, 1, 8, 1024, false>", None, "decode"),
     "decode_b64_mha40_bs32": ("pa::decode_kernel<pa::BF16, 128, 1, 32, 1024, false>", None, "decode"),
     "decode_shared_prefix_plain": ("pa::decode_kernel<pa::BF16, 128, 4, 16, 512, false>", None, "decode"),
-    "decode_shared_prefix_shared": ("pa::shared_decode_kernel<pa::BF16, 128, 4, 16>", None, "shared"),
+    "decode_shared_prefix_shared": ("pa::shared_decode32_kernel<pa::BF16, 128, 4, 16>", None, "shared"),
     "decode_long_ctx": ("pa::decode_kernel<pa::BF16, 128, 8, 16, 512, false>", None, "decode"),
     "append_2048": ("pa::append_kernel", 524288, "cache"),
     "copy_blocks_56": ("pa::copy_blocks_kernel", 229376, "cache"),
