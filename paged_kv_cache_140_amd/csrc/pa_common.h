@@ -81,6 +81,14 @@ __device__ __forceinline__ void store_elem(F16, void* base, int64_t i, float v) 
 }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *static_cast<const uint4*>(p); }
+// The same load marked non-temporal (the K/V stream: each byte is read once
+// per launch, and should not push the block tables and lengths, which every
+// launch reads first, out of the L2).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Two 16-bit floats in one dword, for the packed dot products.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

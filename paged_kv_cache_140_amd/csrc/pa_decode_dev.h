@@ -302,8 +302,8 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
     const int64_t off = (phys * BS + (u % UPB) * U) * static_cast<int64_t>(D * S) + lane_off;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      kr[i] = load16(kbase + off + i * TPW * D * S);
-      vr[i] = load16(vbase + off + i * TPW * D * S);
+      kr[i] = load16_stream(kbase + off + i * TPW * D * S);
+      vr[i] = load16_stream(vbase + off + i * TPW * D * S);
     }
   };
 
