@@ -467,21 +467,6 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
     }
   };
 
-  // Fused: the new token's share of the attention, added by wave 0 of the
-  // partition that holds it, right after the wave's first K/V loads are in
-  // flight (so its own input load overlaps them): a unit whose only live
-  // token is row 0 of its first load, taken from the input.
-  auto add_new_token = [&]() {
-    if constexpr (FUSED) {
-      if (owns_new && wave == 0) {
-        uint4 kxa[NLD], vxa[NLD];
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) kxa[i] = kx, vxa[i] = vx;
-        process(0, kxa, vxa, true, 1);
-      }
-    }
-  };
-
   // Units of this partition: unmasked ones [u_first, u_full), stepping by W
   // per wave, streamed through a ring of RING loads in flight; then at most
   // one masked unit (partly visible, or, fused, the one holding ctx - 1),
@@ -493,6 +478,23 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
   // The partly visible last unit (if this partition has it) is loaded first,
   // by the wave it falls to, and processed last with masking.
   const bool has_tail = u_full < u_stop && u_full >= u_first && (u_full - u_first) % W == 0;
+  // Fused: the new token's share of the attention, added right after the
+  // wave's first K/V loads are in flight (so its own input load overlaps
+  // them): a unit whose only live token is row 0 of its first load, taken
+  // from the input.  With N full units over W waves, waves 0 .. N mod W
+  // (the last of them also takes the masked tail) hold one unit more than
+  // the rest: the new token goes to wave W - 1 when it is one of the rest.
+  const int new_wave = max(0, u_full - u_begin) % W < W - 1 ? W - 1 : 0;
+  auto add_new_token = [&]() {
+    if constexpr (FUSED) {
+      if (owns_new && wave == new_wave) {
+        uint4 kxa[NLD], vxa[NLD];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) kxa[i] = kx, vxa[i] = vx;
+        process(0, kxa, vxa, true, 1);
+      }
+    }
+  };
   uint4 kt[NLD], vt[NLD];
   // The tail's table entry depends on ctx, one more dependent read than the
   // ring's first entries: its loads go after the ring's so that they do not
