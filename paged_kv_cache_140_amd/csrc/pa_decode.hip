@@ -159,8 +159,6 @@ DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx) {
   DecodePlan p;
   const int64_t nblk = ceil_div(max_ctx > 0 ? max_ctx : 1, bs);
   const int64_t pairs = static_cast<int64_t>(B) * H_kv;
-  p.waves = env_waves > 0 ? env_waves : 8;
-  p.waves = p.waves > max_waves_for(G) ? max_waves_for(G) : p.waves;
   if (env_pb > 0) {
     p.blocks_per_part = env_pb;
   } else if (pairs >= cus && nblk <= 256) {
@@ -177,6 +175,13 @@ DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx) {
     p.blocks_per_part = static_cast<int>(pb);
   }
   p.num_parts = static_cast<int>(ceil_div(nblk, p.blocks_per_part));
+  // Waves per workgroup: 4 when every sequence is one partition, 8 for a
+  // split (measured with the K/V loads non-temporal: 4 waves take the B=32
+  // GQA 16/8 step from 16.7 to 16.1 us and the B=64 MHA-40 decode from
+  // 116.5 to 110.2 us; the split decode of 63 contexts of 1k-32k tokens
+  // runs 720 us at 8 waves and 775 us at 4).
+  p.waves = env_waves > 0 ? env_waves : (p.num_parts == 1 ? 4 : 8);
+  p.waves = p.waves > max_waves_for(G) ? max_waves_for(G) : p.waves;
   return p;
 }
 

@@ -3,7 +3,8 @@ benchmark's access-pattern ceiling) reads exactly the visible K/V: the XOR
 of each (sequence, KV head)'s per-wave checksums equals, bit for bit, the
 XOR of the K and V dwords of its visible tokens gathered through the block
 table on the CPU (context lengths that fill whole 16-token units), for
-single-partition and split plans."""
+single-partition and split plans, at 4 and 8 waves per workgroup (the
+library's own choices for one partition and for a split)."""
 
 import numpy as np
 import pytest
@@ -21,9 +22,11 @@ pytestmark = pytest.mark.gpu
     (16, 8, 128, 32, [640, 64, 96], 3),
     (32, 8, 64, 8, [160, 48, 992], 5),
 ])
-def test_gather_checksum_reads_every_visible_token_once(H_q, H_kv, d, bs, lengths, part_blocks, tune):
+@pytest.mark.parametrize("waves", [4, 8])
+def test_gather_checksum_reads_every_visible_token_once(H_q, H_kv, d, bs, lengths, part_blocks, waves, tune):
     import paged_kv_cache_140_amd as pa
 
+    tune(decode_waves=waves)
     if part_blocks:
         tune(decode_part_blocks=part_blocks)
     rng = np.random.default_rng(sum(lengths) + d)
@@ -44,11 +47,11 @@ def test_gather_checksum_reads_every_visible_token_once(H_q, H_kv, d, bs, length
     tab = np.zeros((len(lengths), maxb), dtype=np.int32)
     for i, t in enumerate(tables):
         tab[i, :len(t)] = t
-    say("gather checksum", H_q, H_kv, d, bs, lengths, part_blocks)
+    say("gather checksum", H_q, H_kv, d, bs, lengths, part_blocks, waves)
     cs = pa.pa_gather_checksum(pool, 0, H_q, torch.from_numpy(tab).cuda(),
                                torch.tensor(lengths, dtype=torch.int32).cuda(), max(lengths))
     torch.cuda.synchronize()
-    W = 8  # the decode plan's waves per workgroup
+    W = waves  # the decode plan's waves per workgroup
     got = cs.cpu().numpy().view(np.uint32).reshape(len(lengths), -1, H_kv, W)  # [B][P][H_kv][W]
     got = np.bitwise_xor.reduce(np.bitwise_xor.reduce(got, axis=3), axis=1)  # [B][H_kv]
     for i, n in enumerate(lengths):
