@@ -71,10 +71,15 @@ def mistake_effects(q, k, v, bs, scale):
     P = pb.sum(-1)[..., None]                                     # [H_kv][G][nb][1]
     W = np.einsum("ghbt,gbtd->ghbd", pb, vp.reshape(H_kv, nb, bs, d))
     o = out[:, :, None, :]
-    drop = np.abs((P * o - W) / (1.0 - P)).max(axis=(1, 3))      # [H_kv][nb]
+    # Dropping a block renormalises the rest; dropping a sequence's only
+    # block (P = 1) leaves no key, and the kernel's output is then zero.
+    den = 1.0 - P
+    drop = np.where(den > 0, np.abs((P * o - W) / np.where(den > 0, den, 1.0)), np.abs(o)).max(axis=(1, 3))
     dup = np.abs((W - P * o) / (1.0 + P)).max(axis=(1, 3))
     pl = p[..., -1:]
-    drop_new = np.abs((pl * out - pl * v[:, None, -1, :]) / (1.0 - pl)).max(axis=(1, 2))
+    den_new = 1.0 - pl
+    drop_new = np.where(den_new > 0, np.abs((pl * out - pl * v[:, None, -1, :]) / np.where(den_new > 0, den_new, 1.0)),
+                        np.abs(out)).max(axis=(1, 2))
     k2, v2 = np.roll(k, -1, axis=0), np.roll(v, -1, axis=0)
     wrong = np.abs(np.einsum("ghn,gnd->ghd", _weights(q, k2, scale), v2) - out).max(axis=(1, 2))
     # Counting the only block of a one-block sequence twice changes no
