@@ -14,7 +14,11 @@
 //    one sequence; one K/V read serves all G query heads of the KV head.
 //  * inside a workgroup each wave takes every W-th unit of U tokens
 //    (U <= block size) and keeps the next unit's K and V in flight in
-//    registers while it computes on the current one.
+//    registers while it computes on the current one.  W is 4 when each
+//    sequence is one partition and 8 for a split (plan_decode).
+//  * K and V are loaded non-temporal: each byte is read once per launch,
+//    and the stream should not churn the L2 that every launch first reads
+//    its block tables and lengths from.
 //  * lanes split a token row into 16-byte chunks (LPT lanes per token, one
 //    128-byte line per 8 lanes), so each wave load covers whole lines of one
 //    block; q.k partial sums are combined across the LPT lanes by DPP.
