@@ -454,8 +454,9 @@ def main():
             "B": 32, "H_q": 16, "H_kv": 8, "head_dim": 128, "block_size": 16, "pool_blocks": 1378,
             "layers_rotated": L, "seed": 0,
         },
-        "timing": "HIP graph of K steps replayed 5 times after W eager warmup steps and one untimed replay; "
-                  "each replay timed with events, the median replay reported",
+        "timing": "HIP graph of K steps replayed 11 times (the headline, decode and gather figures; 5 times for the "
+                  "other rows) after W eager warmup steps and one untimed replay; each replay timed with events, "
+                  "the median replay reported",
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "step_ms_spread": spread(step_times),
         "decode_ms_spread": spread(decode_times),

@@ -1,6 +1,11 @@
 """pa_mixed_batch -- a decode batch and causal prefill chunks in one launch
 -- against the oracle, and bit for bit against pa_decode followed by one
-pa_prefill_chunk per chunk on the same inputs."""
+pa_prefill_chunk per chunk on the same inputs.
+
+The mixed kernel's workgroups are 8 waves, so its decode half runs
+pa_decode's plan at 8 waves per workgroup.  pa_decode's default plan takes 4
+waves when it does not split a sequence: the same terms summed in another
+order.  The separate calls here therefore run the 8-wave plan."""
 
 import numpy as np
 import pytest
@@ -14,6 +19,11 @@ from oracle.run import widen
 from pa_inputs import build_scenario
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _eight_wave_decode_plan(tune):
+    tune(decode_waves=8)
 
 
 def _world(rng, dec_lengths, chunk_totals, H_kv, d, bs, dtype):
