@@ -1,6 +1,7 @@
 """pa_decode_shared (shared leading blocks read once for all their sharers)
 against the oracle: the shared-prefix sampling workload in full, beam
-search, and edge shapes; validate mode on bad groups."""
+search, and edge shapes; graph replay and workspace reuse; validate mode
+on bad groups."""
 
 import numpy as np
 import pytest
@@ -122,6 +123,11 @@ CASES = [
     (8, 4, 64, 32, "f16", [(1000, [20, 30]), (40, [1, 2, 3])]),
     (8, 1, 128, 16, "bf16", [(20000, [50, 60]), (9000, [])]),  # long rows: a split suffix
     (16, 8, 128, 16, "bf16", [(100, []), (200, []), (300, [])]),  # no groups at all
+    # every row in a group whose 32-row tile streams its own keys: 41 key
+    # splits of one (group, KV head) to merge
+    (8, 1, 128, 16, "bf16", [(5000, [10, 20, 30, 40])]),
+    (16, 4, 64, 16, "f16", [(1500, [3, 9, 27, 81])]),
+    (32, 8, 128, 16, "bf16", [(2400, [5, 6]), (2500, [1, 2, 3, 4, 5, 6, 7, 8])]),  # two groups, own split counts
 ]
 
 
@@ -166,6 +172,61 @@ def test_shared_decode_edge_shapes(case):
     say("  groups", groups, "max abs err", err, "pa_decode", max_abs_err(f64(ref_out), ref))
     assert err <= TOL[dtype]
     assert max_abs_err(f64(out), f64(ref_out)) <= TOL[dtype]
+
+
+def test_shared_decode_graph_replays_and_workspace_reuse():
+    """One workspace (first filled with 0xff) serves calls with two group
+    lists -- every row in a group whose tile streams its own keys, and the
+    same batch with the first group's rows left to the suffix pass -- and a
+    captured call replayed four times with eager calls between the replays.
+    Every output of the same call is the same bit for bit, and all are within
+    tolerance of the oracle."""
+    import paged_kv_cache_140_amd as pa
+    from paged_kv_cache_140_amd.runner import to_device
+
+    rng = np.random.default_rng(77)
+    H_q, H_kv, d, bs = 32, 8, 128, 16
+    op, gp, tables, lens = _family_world(rng, [(2400, [5, 6]), (2500, [1, 2, 3, 4, 5, 6, 7, 8])], H_kv, d, bs, "bf16")
+    B = len(lens)
+    tab = np.zeros((B, max(len(t) for t in tables)), dtype=np.int32)
+    for i, t in enumerate(tables):
+        tab[i, :len(t)] = t
+    groups = pa.pa_share_groups(tab, np.array(lens, dtype=np.int32), bs)
+    assert groups == [(0, 2, 150), (2, 8, 156)]
+    other = [groups[1]]  # rows 0-1 in no group: suffix pass + merge launch
+    q32 = rng.standard_normal((B, H_q, d)).astype(np.float32) * np.float32(gen.SIGNAL_Q_SCALE)
+    q = to_device(q32, "bf16", "cuda")
+    tab_d, lens_d = torch.from_numpy(tab).cuda(), torch.tensor(lens, dtype=torch.int32).cuda()
+    n = max(pa.pa_decode_shared_workspace_size(gp, B, H_q, max(lens), g) for g in (groups, other))
+    ws = torch.full((n,), 255, dtype=torch.uint8, device="cuda")
+    outs = {k: torch.full_like(q, float("nan")) for k in ("one", "two", "graph")}
+    say("shared decode: graph replays and workspace reuse")
+
+    def call(key, grp):
+        pa.pa_decode_shared(gp, 0, outs[key], q, tab_d, lens_d, max(lens), 0.088, grp, ws)
+
+    call("one", groups)
+    call("two", other)
+    torch.cuda.synchronize()
+    ref = attention.decode(op, 0, widen(q32, "bf16"), tables, lens, 0.088)
+    assert max_abs_err(f64(outs["one"]), ref) <= TOL["bf16"]
+    assert max_abs_err(f64(outs["two"]), ref) <= TOL["bf16"]
+    first = {k: bits(outs[k]) for k in ("one", "two")}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call("graph", groups)
+    for rep in range(4):
+        outs["graph"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(outs["graph"]), first["one"]), f"replay {rep} differs"
+        for key, grp in (("two", other), ("one", groups)):  # eager calls on the same workspace between replays
+            outs[key].fill_(float("nan"))
+            call(key, grp)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(outs[key]), first[key]), f"eager {key} after replay {rep} differs"
+    del g
 
 
 def test_shared_decode_validate_rejects_bad_groups():
