@@ -30,6 +30,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+SHARED_LAYERS = 8  # layers the shared-prefix rows rotate over: 8 x 134 MB, past the 256 MB Infinity Cache
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "paged_kv_cache_140_amd", "csrc")
@@ -57,7 +58,7 @@ COUNTED = {
     "decode_shared_prefix_shared": ("pa::shared_decode32_kernel<pa::BF16, 128, 4, 16>", None, "shared"),
     "decode_long_ctx": ("pa::decode_kernel<pa::BF16, 128, 8, 16, 512, false>", None, "decode"),
     "append_2048": ("pa::append_kernel", 524288, "cache"),
-    "copy_blocks_56": ("pa::copy_blocks_kernel", 229376, "cache"),
+    "copy_blocks_56": ("pa::copy_blocks_kernel", 1835008, "cache"),  # 56 pairs x 8 layers
     "prefill_chunk_1024": ("pa::prefill_chunk_kernel<pa::BF16, 128, 8, 16>", 131072, "prefill", "unsplit"),
 }
 HEADLINE = "decode_b32_gqa16x8_fused"
@@ -553,20 +554,31 @@ def main():
     # ---------------------------------------------------------- other rows
     if not args.no_rows:
         rows = {}
+        # The workload's pool (134 MB per layer) fits the 256 MB Infinity
+        # Cache, so, as for the headline, each step works on the next of
+        # SHARED_LAYERS layers and reads its K/V cold.
         scn4 = build_scenario(4, 0)
-        g4 = DeviceRun(scn4, device=dev, fill="randn")
+        g4 = DeviceRun(scn4, device=dev, num_layers=SHARED_LAYERS, fill="randn")
         g4.run_setup()
         tail = g4.prepare(scn4.steps[0])
         dec = g4.prepare(scn4.steps[1], shared=True)
         nrep = 50
-        ms_copy = time_loop(torch, lambda i: g4.launch(tail, do_append=False), nrep, 5)
-        ms_tail = time_loop(torch, lambda i: g4.launch(tail, do_copy=False), nrep, 5)
-        ms_d4 = time_loop(torch, lambda i: g4.launch(dec, do_copy=False, do_append=False), nrep, 5)
-        ms_d4s = time_loop(torch, lambda i: g4.launch(dec, do_copy=False, do_append=False, shared=True), nrep, 5)
+
+        def on_layer(fn):
+            def f(i):
+                g4.layer = i % SHARED_LAYERS
+                fn()
+            return f
+        ms_copy = time_loop(torch, on_layer(lambda: g4.launch(tail, do_append=False)), nrep, 5)
+        ms_tail = time_loop(torch, on_layer(lambda: g4.launch(tail, do_copy=False)), nrep, 5)
+        ms_d4 = time_loop(torch, on_layer(lambda: g4.launch(dec, do_copy=False, do_append=False)), nrep, 5)
+        ms_d4s = time_loop(torch, on_layer(lambda: g4.launch(dec, do_copy=False, do_append=False, shared=True)),
+                           nrep, 5)
         L4 = dec.lens.cpu().numpy()
-        copy_b = 2 * tail.n_pairs * 1 * 2 * 8 * 16 * 128 * 2
+        copy_b = 2 * tail.n_pairs * SHARED_LAYERS * 2 * 8 * 16 * 128 * 2
         uniq = 8 * 3000 * 8 * 128 * 2 * 2 + 64 * (int(L4[0]) - 3000) * 8 * 128 * 2 * 2
-        rows["cow_copy_blocks"] = {"workload": "shared-prefix sampling: 56 copy-on-write block copies",
+        rows["cow_copy_blocks"] = {"workload": f"shared-prefix sampling: 56 copy-on-write block copies, in each of "
+                                               f"the pool's {SHARED_LAYERS} layers",
                                    "ms": round(ms_copy, 5), "GBps": round(copy_b / (ms_copy * 1e-3) / 1e9, 1),
                                    **traffic_fields("copy_blocks_56", copy_b)}
         rows["append_2048"] = {"workload": "shared-prefix sampling: 64 x 32-token tails",
@@ -575,7 +587,8 @@ def main():
                                **traffic_fields("append_2048", append_bytes(2048, 8, 128, 2))}
         rows["decode_shared_prefix"] = {
             "workload": "64 samples sharing 8 x 3,000-token prefixes, ctx 3,034; pa_decode_shared (8 groups of 8 "
-                        "rows sharing 187 blocks, read once per group) against pa_decode (read once per sample)",
+                        "rows sharing 187 blocks, read once per group) against pa_decode (read once per sample); "
+                        f"{SHARED_LAYERS} layers rotated",
             "ms": round(ms_d4s, 5),
             "unique_GBps": round(uniq / (ms_d4s * 1e-3) / 1e9, 1),
             "unique_hbm_frac": round(uniq / (ms_d4s * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -779,7 +792,9 @@ def prefix_cache_row(torch, pa, np):
     t_miss = (time.perf_counter() - t0) / reps
     assert hit == 2992
 
-    pool = pa.KVPool(1, H_kv, 200, bs, d, "bf16", device="cuda")
+    # 28 layers of 13 MB, one per timed call, so that the K/V come from HBM
+    layers = 28
+    pool = pa.KVPool(layers, H_kv, 200, bs, d, "bf16", device="cuda")
     pool.k.normal_()
     pool.v.normal_()
     table = torch.from_numpy(rng.permutation(200)[:190].astype(np.int32)).cuda()
@@ -787,11 +802,12 @@ def prefix_cache_row(torch, pa, np):
     qf = torch.randn(3032, H_q, d, device="cuda").to(torch.bfloat16)
     of = torch.empty_like(qf)
     qh, oh = qf[-40:].contiguous(), torch.empty_like(qf[-40:])
-    ms_full = time_loop(torch, lambda i: pa.pa_prefill_chunk(pool, 0, of, qf, table, 0, scale), 20, 3)
+    ms_full = time_loop(torch, lambda i: pa.pa_prefill_chunk(pool, i % layers, of, qf, table, 0, scale), 20, 3)
     ws = pa.prefill_workspace(pool, 40, H_q, 2992)
-    ms_hit = time_loop(torch, lambda i: pa.pa_prefill_chunk(pool, 0, oh, qh, table, 2992, scale, ws), 20, 3)
-    ms_hit_one = time_loop(torch, lambda i: pa.pa_prefill_chunk(pool, 0, oh, qh, table, 2992, scale), 20, 3)
-    return {"workload": "3,000-token shared prefix + 32-token tail per request, block 16, GQA 32/8, d 128",
+    ms_hit = time_loop(torch, lambda i: pa.pa_prefill_chunk(pool, i % layers, oh, qh, table, 2992, scale, ws), 20, 3)
+    ms_hit_one = time_loop(torch, lambda i: pa.pa_prefill_chunk(pool, i % layers, oh, qh, table, 2992, scale), 20, 3)
+    return {"workload": "3,000-token shared prefix + 32-token tail per request, block 16, GQA 32/8, d 128, "
+                        f"{layers} layers rotated",
             "hit_tokens": hit, "host_admit_hit_us": round(t_hit * 1e6, 1),
             "host_admit_miss_us": round(t_miss * 1e6, 1),
             "prefill_whole_prompt_ms": round(ms_full, 5), "prefill_after_hit_ms": round(ms_hit, 5),
