@@ -316,7 +316,7 @@ def main():
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the hot path is measured on one GPU's share; "
+        print(json.dumps({"error": "the benchmark runs on one GPU only: the hot path is measured on one GPU's share; "
                                    "run with --gpus 1"}), flush=True)
         return 2
 
