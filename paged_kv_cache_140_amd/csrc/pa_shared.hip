@@ -118,27 +118,55 @@ __global__ void __launch_bounds__(kPrefillThreads)
 // LDS, with no barrier between steps.  Every global load goes straight into
 // LDS (global_load_lds_dwordx4) and is waited for by explicit counts, so
 // that the compiler's own load tracking never makes a step wait for the
-// step behind it.  K and V tiles use the prefill tile's LDS layout, so the
-// MFMA operand reads and the transposing V reads are the ones it uses.  At
-// the end the 4 waves merge their (m, l, O) through LDS into one partial.
+// step behind it.  Each load reads whole 128-byte lines (8 rows of one
+// line-wide part), non-temporal, into a swizzled layout on which the MFMA
+// operand reads and the transposing V reads stay on distinct banks.  At the
+// end the 4 waves merge their (m, l, O) through LDS into one partial.
 constexpr int kShWaves = 4;
 constexpr int kShThreads = 64 * kShWaves;
 constexpr int kShKT = 32;     // keys per step
 constexpr int kShStages = 2;  // steps in flight per wave
 
+// LDS layout of a 32-row K, V or q tile: the row's bytes [128 p, 128 p +
+// 128) (one 128-byte line of global memory) lie in part p, 4 KiB of 32
+// rows x 128 bytes, and inside a row's 128 bytes the 16-byte chunk c sits
+// at position c ^ sw(row).  Each direct load fills 8 rows of one part:
+// lane l lands at byte 16 l (row 8 i + l / 8, position l % 8), so every
+// load reads 8 whole lines of global memory.  The swizzle keeps the MFMA
+// operand reads (16 rows, one chunk each, per pass) and the transposing V
+// reads (32 lanes: 4 rows x 8 chunk halves per pass) on distinct banks.
 template <int D>
 struct ShLayout {
   static constexpr int ROWB = D * 2;                 // bytes of a K/V/q row
   static constexpr int TILE = kShKT * ROWB;          // one 32-row tile
-  static constexpr int COLS = ROWB / 64;             // 64-byte columns
+  static constexpr int PARTS = ROWB / 128;           // 128-byte parts of a row
+  static constexpr int PART = kShKT * 128;           // bytes of one part
   static constexpr int LOADS = TILE / 1024;          // 1 KiB direct loads per tile
   static constexpr int STAGE = 2 * TILE;             // K then V
   static constexpr int RING = kShStages * STAGE;     // one wave's ring
   static constexpr int QOFF = kShWaves * RING;       // the 32 query rows
   static constexpr int BYTES = QOFF + TILE;
-  static_assert(LOADS == 2 * COLS, "two 16-row groups per tile");
+  static_assert(PARTS >= 1 && LOADS == 4 * PARTS, "four 8-row loads per part");
   static_assert(32 * D * 4 + 2 * 32 * 4 <= RING, "a wave's (o, m, l) fit its ring");
 };
+__device__ __forceinline__ int sh_swizzle(int row) {
+  const int x = (row >> 1) & 7;  // bit-reversed: rows 2 apart land 4 chunks apart
+  return ((x & 1) << 2) | (x & 2) | (x >> 2);
+}
+// Byte of the tile at which row `row`, byte `b` of the row (16-byte chunk
+// units and the offset inside the chunk) is stored.
+__device__ __forceinline__ int sh_off(int row, int b) {
+  return (b >> 7) * (kShKT * 128) + row * 128 + ((((b >> 4) & 7) ^ sh_swizzle(row)) << 4) + (b & 15);
+}
+
+// global_load_lds_dwordx4 with the non-temporal bit: K and V of the tile are
+// read once per launch, and every 128-byte line by one load.
+__device__ __forceinline__ void load_to_lds_stream(const char* src, char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(m0) : "memory");
+#endif
+}
 
 // s_waitcnt vmcnt(n), expcnt and lgkmcnt at their maxima (gfx9 encoding).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -174,26 +202,25 @@ __device__ __forceinline__ void prefix_tile32(int g, int n_rows, int v_lo, int v
   char* ring = lds + wave * L::RING;
   char* qt = lds + L::QOFF;
 
-  // Direct loads: load i of a tile fills 16 rows (group rg = i / COLS) of
-  // one 64-byte column (i % COLS); lane l lands at byte 16 l: row 16 rg +
-  // l / 4, rotated chunk position l % 4 (the prefill tile's layout).
-  const int lrow = lane >> 2;
-  auto chunk_of = [&](int row) { return ((lane & 3) ^ ((row >> 2) & 3)) * 16; };
+  // Direct loads: load (p, i) of a tile fills rows 8 i + [0, 8) of part p;
+  // lane l takes row 8 i + l / 8 and the row's chunk 8 p + ((l % 8) ^
+  // sw(row)), which lands at byte 16 l of the load's 1 KiB.
+  const int lrow = lane >> 3;
+  auto chunk_byte = [&](int row, int p) { return p * 128 + (((lane & 7) ^ sh_swizzle(row)) << 4); };
 
   // The 32 query rows, loaded once per workgroup: wave w issues loads
   // w, w + 4, ... of the q tile.  Rows past the group's are clamped (never
   // stored).
 #pragma unroll
-  for (int i = wave; i < L::LOADS; i += kShWaves) {
-    const int rg = i / L::COLS, col = i % L::COLS;
-    const int r = min(rg * 16 + lrow, rows - 1);
-    const char* src = q + ((static_cast<int64_t>(r / G) * H_q + g * G + r % G) * D) * 2 + col * 64 +
-                      chunk_of(rg * 16 + lrow);
-    load_to_lds(src, qt + col * (KT * 64) + rg * 1024);
+  for (int n = wave; n < L::LOADS; n += kShWaves) {
+    const int p = n / 4, i = n % 4;
+    const int r = min(i * 8 + lrow, rows - 1);
+    const char* src = q + ((static_cast<int64_t>(r / G) * H_q + g * G + r % G) * D) * 2 + chunk_byte(i * 8 + lrow, p);
+    load_to_lds(src, qt + p * L::PART + i * 1024);
   }
 
   // Steps of this wave: steps v_lo + wave, v_lo + wave + 4, ... (an index
-  // past the wave's last is clamped to it: its loads repeat, unused).
+  // past the wave's last is clamped to it; no loads are issued for it).
   const int nsteps = v_hi - v_lo;
   const int nw = nsteps > wave ? (nsteps - wave + kShWaves - 1) / kShWaves : 0;
   const int P = (S + KT - 1) / KT;
@@ -229,18 +256,18 @@ __device__ __forceinline__ void prefix_tile32(int g, int n_rows, int v_lo, int v
     char* kt = ring + slot * L::STAGE;
     char* vt = kt + L::TILE;
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      // A lane's 8 or 16 rows sit in one block (S is a multiple of the
-      // block size, steps start 32 keys apart): past the limit, the spare.
-      const int first = st.k0 + rg * 16 + ((BS >= 16 || lrow < 8) ? 0 : 8);
-      const bool past = first >= st.lim;
-      const int key = past ? 0 : min(st.k0 + rg * 16 + lrow, st.lim - 1);
-      const int64_t blk = past ? spare : ((BS >= 16 || lrow < 8) ? st.b[rg][0] : st.b[rg][1]);
-      const int64_t off = (blk * BS + (key & (BS - 1))) * L::ROWB + chunk_of(rg * 16 + lrow);
+    for (int i = 0; i < 4; ++i) {
+      // A load's 8 rows sit in one block (S is a multiple of the block
+      // size, steps start 32 keys apart): past the limit, the spare.
+      const bool past = st.k0 + i * 8 >= st.lim;
+      const int key = past ? 0 : min(st.k0 + i * 8 + lrow, st.lim - 1);
+      const int64_t blk = past ? spare : st.b[i >> 1][i & 1];
+      const int64_t off = (blk * BS + (key & (BS - 1))) * L::ROWB;
 #pragma unroll
-      for (int col = 0; col < L::COLS; ++col) {
-        load_to_lds(kbase + off + col * 64, kt + col * (KT * 64) + rg * 1024);
-        load_to_lds(vbase + off + col * 64, vt + col * (KT * 64) + rg * 1024);
+      for (int p = 0; p < L::PARTS; ++p) {
+        const int cb = chunk_byte(i * 8 + lrow, p);
+        load_to_lds_stream(kbase + off + cb, kt + p * L::PART + i * 1024);
+        load_to_lds_stream(vbase + off + cb, vt + p * L::PART + i * 1024);
       }
     }
   };
@@ -257,28 +284,40 @@ __device__ __forceinline__ void prefix_tile32(int g, int n_rows, int v_lo, int v
   int limc = 0;
   if (nw > 0) {
     issue(fetch(0), 0);
-    issue(fetch(1), 1);
+    if (nw > 1) issue(fetch(1), 1);
     next = fetch(2);
     limc = lim_of(0);
   }
   // q landed (each wave waits for its own q loads; the steps behind them may
   // stay in flight), then the workgroup's q loads are all visible.
-  if (nw > 0) {
+  if (nw > 1) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPS));
+  } else if (nw == 1) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS));
   } else {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
   barrier_keep_loads();
 
+  // MFMA operand of K and q: row li, chunk 2 ks + h, at a per-lane offset
+  // for each ks % 4 plus part ks / 4.
   vec qb[KS];
-  const int kb_even = tile_off<KT>(li, h), kb_odd = tile_off<KT>(li, 2 + h);
+  int kb[4];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qb[ks] = *reinterpret_cast<const vec*>(qt + (ks >> 1) * (KT * 64) + ((ks & 1) ? kb_odd : kb_even));
-  // transposing V reads: as the prefill tile's, for one 32-key tile
+  for (int k = 0; k < 4; ++k) kb[k] = sh_off(li, (2 * k + h) * 16);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const vec*>(qt + (ks >> 2) * L::PART + kb[ks & 3]);
+  // Transposing V reads of a 16-key slice s2 and dims dt * 32 + [0, 32):
+  // this lane, as source lane 4 k4 + q4 of its 16-lane group g16, addresses
+  // 4 dims of row s2 * 16 + vrow (+ 8), at a per-lane offset for each
+  // (row half, dt % 2) plus part dt / 2 and 16 rows per s2.
   const int g16 = lane >> 4, k4 = (lane >> 2) & 3, q4 = lane & 3;
   const int vrow = 4 * (g16 >> 1) + k4, vch = (g16 & 1) * 2 + (q4 >> 1);
-  const int vb_lo = tile_off<KT>(vrow, vch) + (q4 & 1) * 8, vb_hi = tile_off<KT>(vrow + 8, vch) + (q4 & 1) * 8;
+  int vb[2][2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2) vb[hi][d2] = sh_off(vrow + 8 * hi, d2 * 64 + vch * 16 + (q4 & 1) * 8);
 
   float m = -INFINITY, lsum = 0.0f;
   floatx16_t o[DT];
@@ -290,29 +329,33 @@ __device__ __forceinline__ void prefix_tile32(int g, int n_rows, int v_lo, int v
     const int slot = j & 1;
     const char* kt = ring + slot * L::STAGE;
     const char* vt = kt + L::TILE;
-    // step j has landed; step j + 1 (LPS loads) may still be in flight
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS));
+    // step j has landed; step j + 1 (LPS loads), if any, may still be in
+    // flight
+    if (j + 1 < nw) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
     vec ka[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      ka[ks] = *reinterpret_cast<const vec*>(kt + (ks >> 1) * (KT * 64) + ((ks & 1) ? kb_odd : kb_even));
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = *reinterpret_cast<const vec*>(kt + (ks >> 2) * L::PART + kb[ks & 3]);
     vec va[2][DT];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const char* vs = vt + (s2 * 16) * 64 + dt * (KT * 64);
-        const uint2 lo = lds_read_tr(vs + vb_lo);
-        const uint2 hi = lds_read_tr(vs + vb_hi);
+        const char* vs = vt + s2 * 16 * 128 + (dt >> 1) * L::PART;
+        const uint2 lo = lds_read_tr(vs + vb[0][dt & 1]);
+        const uint2 hi = lds_read_tr(vs + vb[1][dt & 1]);
         va[s2][dt] = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
     // Every read of this slot is back before its refill (step j + 2) lands
-    // in it; the refill index is clamped, so every wave issues the same
-    // number of loads per step and the counts above stay exact.
+    // in it.  A wave's last two steps refill nothing, so a step's wait
+    // above leaves one step in flight, or none at the last.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_sched_barrier(0);
-    issue(next, slot);
+    if (j + 2 < nw) issue(next, slot);
     next = fetch(j + 3);
     __builtin_amdgcn_sched_barrier(0);
     const int lim = limc;
