@@ -297,9 +297,15 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
   const char* vbase = pool_v + layer_off + static_cast<int64_t>(g) * head_stride;
   const int lane_off = (r * D + c * VEC) * S;
 
-  auto load_unit = [&](int u, uint4* kr, uint4* vr, int32_t phys_id) {
-    const int64_t phys = __builtin_amdgcn_readfirstlane(phys_id);
-    const int64_t off = (phys * BS + (u % UPB) * U) * static_cast<int64_t>(D * S) + lane_off;
+  // A placeholder load (a ring slot past the wave's last unit, or the tail
+  // slot of a wave without the tail) keeps the count of loads in flight
+  // fixed, so the waits stay exact.  It reads the head's block 0 rather than
+  // re-reading a unit of K/V: every placeholder of the launch reads the same
+  // few lines, which stay in L2, where a re-read of the non-temporal stream
+  // would go back to HBM.
+  auto load_unit = [&](int u, uint4* kr, uint4* vr, int32_t phys_id, bool dummy) {
+    const int64_t phys = dummy ? 0 : __builtin_amdgcn_readfirstlane(phys_id);
+    const int64_t off = (phys * BS + (dummy ? 0 : u % UPB) * U) * static_cast<int64_t>(D * S) + lane_off;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       kr[i] = load16_stream(kbase + off + i * TPW * D * S);
@@ -498,23 +504,22 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
   uint4 kt[NLD], vt[NLD];
   // The tail's table entry depends on ctx, one more dependent read than the
   // ring's first entries: its loads go after the ring's so that they do not
-  // hold the ring's back.  Unconditional (a wave without the tail re-reads
-  // its partition's first unit, a cache hit): every wave then has the same
-  // loads in flight, and the waits below stay exact.
+  // hold the ring's back.  Unconditional (a wave without the tail issues
+  // placeholder loads): every wave then has the same loads in flight, and
+  // the waits below stay exact.
   auto load_tail = [&]() __attribute__((always_inline)) {
     const int ut = has_tail ? u_full : u_begin;
-    load_unit(ut, kt, vt, btrow[ut / UPB]);
+    load_unit(ut, kt, vt, btrow[ut / UPB], !has_tail);
   };
   if (n_w > 0) {
-    // Refills are unconditional, with the unit index clamped to the wave's
-    // last one (a cache hit), so each ring slot stays in fixed registers and
-    // no load ever waits for a later one.  A first-round slot past the
-    // wave's units re-reads its first unit, whose table entry is at hand.
+    // Refills are unconditional (past the wave's last unit, placeholder
+    // loads), so each ring slot stays in fixed registers and no load ever
+    // waits for a later one.
     uint4 kr[RING][NLD], vr[RING][NLD];
 #pragma unroll
     for (int p = 0; p < RING; ++p) {
       const bool live = p < n_w;
-      load_unit(live ? u_first + p * W : u_first, kr[p], vr[p], live ? ph[p] : ph[0]);
+      load_unit(live ? u_first + p * W : u_first, kr[p], vr[p], live ? ph[p] : ph[0], !live);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_tail();
@@ -531,7 +536,7 @@ __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, in
         // ever waits for the oldest slot.
         __builtin_amdgcn_sched_barrier(0);
         const int un = u_first + min(idx + RING, n_w - 1) * W;
-        load_unit(un, kr[p], vr[p], btrow[un / UPB]);
+        load_unit(un, kr[p], vr[p], btrow[un / UPB], idx + RING >= n_w);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
