@@ -14,8 +14,7 @@
 //    one sequence; one K/V read serves all G query heads of the KV head.
 //  * inside a workgroup each wave takes every W-th unit of U tokens
 //    (U <= block size) and keeps the next unit's K and V in flight in
-//    registers while it computes on the current one.  W is 4 when each
-//    sequence is one partition and 8 for a split (plan_decode).
+//    registers while it computes on the current one.  W is 8 (plan_decode).
 //  * K and V are loaded non-temporal: each byte is read once per launch,
 //    and the stream should not churn the L2 that every launch first reads
 //    its block tables and lengths from.
@@ -179,12 +178,12 @@ DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx) {
     p.blocks_per_part = static_cast<int>(pb);
   }
   p.num_parts = static_cast<int>(ceil_div(nblk, p.blocks_per_part));
-  // Waves per workgroup: 4 when every sequence is one partition, 8 for a
-  // split (measured with the K/V loads non-temporal: 4 waves take the B=32
-  // GQA 16/8 step from 16.7 to 16.1 us and the B=64 MHA-40 decode from
-  // 116.5 to 110.2 us; the split decode of 63 contexts of 1k-32k tokens
-  // runs 720 us at 8 waves and 775 us at 4).
-  p.waves = env_waves > 0 ? env_waves : (p.num_parts == 1 ? 4 : 8);
+  // Waves per workgroup: 8 (with the K/V loads non-temporal and the
+  // placeholder refills reading block 0, 8 waves against 4: the B=32 GQA
+  // 16/8 step 16.0 against 16.1 us, the B=64 MHA-40 decode 104.2 against
+  // 105.0 us, the split decode of 63 contexts of 1k-32k tokens 740 against
+  // 797 us).
+  p.waves = env_waves > 0 ? env_waves : 8;
   p.waves = p.waves > max_waves_for(G) ? max_waves_for(G) : p.waves;
   return p;
 }

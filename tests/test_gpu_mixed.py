@@ -3,9 +3,9 @@
 pa_prefill_chunk per chunk on the same inputs.
 
 The mixed kernel's workgroups are 8 waves, so its decode half runs
-pa_decode's plan at 8 waves per workgroup.  pa_decode's default plan takes 4
-waves when it does not split a sequence: the same terms summed in another
-order.  The separate calls here therefore run the 8-wave plan."""
+pa_decode's plan at 8 waves per workgroup; the separate calls here pin that
+plan (the library's default), since another wave count sums the same terms
+in another order."""
 
 import numpy as np
 import pytest
