@@ -147,7 +147,9 @@ struct ShLayout {
   static constexpr int QOFF = kShWaves * RING;       // the 32 query rows
   static constexpr int BYTES = QOFF + TILE;
   static_assert(PARTS >= 1 && LOADS == 4 * PARTS, "four 8-row loads per part");
-  static_assert(32 * D * 4 + 2 * 32 * 4 <= RING, "a wave's (o, m, l) fit its ring");
+  static constexpr int OS = D + 4;                   // floats per row of a wave's staged o (a 16-byte pad:
+                                                      // the rows' writes fall on distinct banks)
+  static_assert(32 * OS * 4 + 2 * 32 * 4 <= RING, "a wave's (o, m, l) fit its ring");
 };
 __device__ __forceinline__ int sh_swizzle(int row) {
   const int x = (row >> 1) & 7;  // bit-reversed: rows 2 apart land 4 chunks apart
@@ -412,16 +414,17 @@ __device__ __forceinline__ void prefix_tile32(int g, int n_rows, int v_lo, int v
   }
 
   // Merge the 4 waves through LDS (each wave's ring, once its own loads
-  // have all landed): o as [32 rows][D] fp32, then m and l per row.
+  // have all landed): o as [32 rows][D] fp32, rows L::OS floats apart, then
+  // m and l per row.
   const float lt = sum_halves(lsum);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   float* wo = reinterpret_cast<float*>(ring);
-  float* wm = wo + 32 * D;
+  float* wm = wo + 32 * L::OS;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
-      *reinterpret_cast<float4*>(wo + li * D + dt * 32 + 8 * jj + 4 * h) =
+      *reinterpret_cast<float4*>(wo + li * L::OS + dt * 32 + 8 * jj + 4 * h) =
           make_float4(o[dt][4 * jj], o[dt][4 * jj + 1], o[dt][4 * jj + 2], o[dt][4 * jj + 3]);
   if (h == 0) {
     wm[li] = m;
@@ -433,7 +436,7 @@ __device__ __forceinline__ void prefix_tile32(int g, int n_rows, int v_lo, int v
     float mw[kShWaves], mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kShWaves; ++w) {
-      mw[w] = reinterpret_cast<const float*>(lds + w * L::RING)[32 * D + r];
+      mw[w] = reinterpret_cast<const float*>(lds + w * L::RING)[32 * L::OS + r];
       mx = fmaxf(mx, mw[w]);
     }
     const float msafe = (mx == -INFINITY) ? 0.0f : mx;
@@ -442,8 +445,8 @@ __device__ __forceinline__ void prefix_tile32(int g, int n_rows, int v_lo, int v
     for (int w = 0; w < kShWaves; ++w) {
       const float* base = reinterpret_cast<const float*>(lds + w * L::RING);
       const float wt = __builtin_amdgcn_exp2f(mw[w] - msafe);
-      acc += base[r * D + e] * wt;
-      lw += base[32 * D + 32 + r] * wt;
+      acc += base[r * L::OS + e] * wt;
+      lw += base[32 * L::OS + 32 + r] * wt;
     }
     const int64_t row = static_cast<int64_t>(r / G) * H_q + g * G + r % G;
     ws_o[row * D + e] = acc;
