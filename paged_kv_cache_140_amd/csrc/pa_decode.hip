@@ -100,10 +100,10 @@ __global__ void __launch_bounds__(MAXT)
 template <typename E, int D>
 __global__ void __launch_bounds__(D)
     decode_merge_kernel(void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
-                        const int32_t* __restrict__ context_lens, int32_t H_q, int32_t num_parts,
+                        const int32_t* __restrict__ context_lens, int32_t H_q, int32_t H_kv, int32_t num_parts,
                         int32_t part_tokens) {
   extern __shared__ float w_lds[];  // [num_parts] weights, then [1] total
-  const int64_t bh = blockIdx.x;
+  const int64_t bh = merge_row(blockIdx.x, H_q, H_kv);
   const int b = static_cast<int>(bh / H_q);
   const int e = threadIdx.x;
   const int ctx = context_lens[b];
@@ -204,13 +204,13 @@ Workspace carve(void* ws, const DecodePlan& pl, int B, int H_kv, int H_q) {
 }
 
 void launch_decode_merge(int dtype, int D, void* out, const Workspace& ws, const int32_t* ctx, int32_t B, int32_t H_q,
-                         const DecodePlan& pl, int bs, hipStream_t stream) {
+                         int32_t H_kv, const DecodePlan& pl, int bs, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(B) * H_q);
   const size_t lds = pl.num_parts * sizeof(float);
   const int pt = pl.blocks_per_part * bs;
 #define PA_MERGE(E_, D_) \
   hipLaunchKernelGGL((decode_merge_kernel<E_, D_>), grid, dim3(D_), lds, stream, out, ws.ml, ws.acc, ctx, H_q, \
-                     pl.num_parts, pt)
+                     H_kv, pl.num_parts, pt)
   if (dtype == PA_F32 && D == 64) PA_MERGE(F32, 64);
   if (dtype == PA_F32 && D == 128) PA_MERGE(F32, 128);
   if (dtype == PA_BF16 && D == 64) PA_MERGE(BF16, 64);
@@ -241,7 +241,7 @@ static void launch_decode(const pa_kv_pool* pool, int32_t layer, void* out, cons
                      static_cast<const char*>(q), out, bt, max_blocks, ctx, scale_log2, H_q, pl.blocks_per_part,
                      pl.num_parts, pl.waves, ws.ml, ws.acc, static_cast<const char*>(nt.k), static_cast<const char*>(nt.v),
                      nt.slots);
-  if (pl.num_parts > 1) launch_decode_merge(pool->dtype, D, out, ws, ctx, B, H_q, pl, BS, stream);
+  if (pl.num_parts > 1) launch_decode_merge(pool->dtype, D, out, ws, ctx, B, H_q, pool->num_kv_heads, pl, BS, stream);
 }
 
 using DecodeFn = void (*)(const pa_kv_pool*, int32_t, void*, const void*, int32_t, int32_t, const int32_t*, int32_t,

@@ -75,7 +75,7 @@ int decode_workspace_check(const std::string& who, const DecodePlan& pl, const p
                            int32_t H_q, void* workspace, size_t workspace_bytes, Workspace* ws);
 // Enqueues the kernel that merges the partitions of a split decode.
 void launch_decode_merge(int dtype, int D, void* out, const Workspace& ws, const int32_t* ctx, int32_t B,
-                         int32_t H_q, const DecodePlan& pl, int bs, hipStream_t stream);
+                         int32_t H_q, int32_t H_kv, const DecodePlan& pl, int bs, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill
 // Host-side checks of a prefill chunk's arguments (PA_OK for T == 0).

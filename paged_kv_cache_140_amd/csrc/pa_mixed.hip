@@ -295,7 +295,8 @@ extern "C" int pa_mixed_batch(const pa_kv_pool* pool, int32_t layer, void* dec_o
   }
   fn(pool, m, stream);
   if (B > 0 && m.pl.num_parts > 1)
-    launch_decode_merge(pool->dtype, pool->head_dim, dec_out, m.ws, context_lens, B, H_q, m.pl, pool->block_size,
+    launch_decode_merge(pool->dtype, pool->head_dim, dec_out, m.ws, context_lens, B, H_q, pool->num_kv_heads, m.pl,
+                        pool->block_size,
                         stream);
   return check_launch("pa_mixed_batch");
 }
