@@ -121,4 +121,17 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// The row (sequence or position, query head) a merge workgroup takes, in an
+// order that runs KV head g's rows on XCD g mod 8 (workgroup L runs on XCD
+// L mod 8): the decode, shared-prefix and split prefill kernels run KV head
+// g's workgroups there too (KV head fastest in their grids), so with H_kv a
+// multiple of 8 the merge reads the partials from the L2 they were written
+// through.
+__device__ __forceinline__ int64_t merge_row(int64_t L, int32_t H_q, int32_t H_kv) {
+  const int G = H_q / H_kv;
+  const int g = static_cast<int>(L % H_kv);
+  const int64_t rest = L / H_kv;
+  return (rest / G) * H_q + g * G + rest % G;
+}
+
 }  // namespace pa

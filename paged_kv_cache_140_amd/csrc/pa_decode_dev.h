@@ -186,18 +186,6 @@ __device__ __forceinline__ void gather_heads(const uint32_t* own, uint32_t* all)
 // instead of attended to (no q, no softmax, no output).  Each wave writes
 // its checksum (uint32) to ws_ml at ((b * num_parts + part) * H_kv + g) * W
 // + wave.  It measures what the decode's access pattern alone can stream.
-// The (sequence, query head) row a merge workgroup takes, in an order that
-// runs KV head g's rows on XCD g mod 8 (workgroup L runs on XCD L mod 8):
-// the decode and shared-prefix kernels run KV head g's workgroups there too
-// (KV head fastest in their grids), so with H_kv a multiple of 8 the merge
-// reads the partials from the L2 they were written through.
-__device__ __forceinline__ int64_t merge_row(int64_t L, int32_t H_q, int32_t H_kv) {
-  const int G = H_q / H_kv;
-  const int g = static_cast<int>(L % H_kv);
-  const int64_t rest = L / H_kv;
-  return (rest / G) * H_q + g * G + rest % G;
-}
-
 template <typename E, int D, int G, int BS, bool FUSED, bool SUFFIX = false, bool CHECKSUM = false>
 __device__ __forceinline__ void decode_body(int W, int g, int part, int H_kv, int b, float* __restrict__ smem,
                                             char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off,

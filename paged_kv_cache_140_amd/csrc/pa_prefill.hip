@@ -51,11 +51,25 @@ __global__ void __launch_bounds__(kPrefillThreads)
                          float* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(1024))) PrefillLds<D> lds;
   // One (work item, key split) per workgroup; gridDim.x = ntiles * H_kv *
-  // num_splits.  Consecutive ids take the items of one split, so the tiles
-  // of one KV head, which read the same keys, share an XCD's L2.
-  const int w = xcd_contiguous(blockIdx.x, gridDim.x);
+  // num_splits.  Unsplit, consecutive ids take the items of one KV head, so
+  // its tiles, which read the same keys, share an XCD's L2.  Split, the KV
+  // head is fastest: head g's tiles and splits run on XCD g mod 8 (with H_kv
+  // a multiple of 8), where the merge takes head g's rows and finds their
+  // partials in that XCD's L2.
   const int items = gridDim.x / num_splits;
-  const int split = w / items;
+  int w, split;
+  if (num_splits > 1) {
+    constexpr int TP = kRowsPerWave * kPrefillWaves / G;
+    const int ntiles = (T + TP - 1) / TP;
+    const int H_kv = items / ntiles;
+    const int L = blockIdx.x;
+    const int rest = L / H_kv;
+    w = (L % H_kv) * ntiles + rest % ntiles;
+    split = rest / ntiles;
+  } else {
+    w = xcd_contiguous(blockIdx.x, gridDim.x);
+    split = 0;
+  }
   float* wo = nullptr;
   float* wml = nullptr;
   if (num_splits > 1) {
@@ -78,7 +92,7 @@ __global__ void __launch_bounds__(D)
                          int32_t T, int32_t H_q, int32_t G, int32_t ctx_before, int32_t num_splits,
                          int32_t steps_per_split) {
   extern __shared__ float wt[];  // [num_splits] weights, then the total weight
-  const int64_t row = blockIdx.x;  // pos * H_q + head
+  const int64_t row = merge_row(blockIdx.x, H_q, H_q / G);  // pos * H_q + head, KV head g's rows on XCD g mod 8
   const int pos = static_cast<int>(row / H_q);
   const int e = threadIdx.x;
   const int TP = kRowsPerWave * kPrefillWaves / G;
