@@ -126,7 +126,9 @@ __device__ __forceinline__ float group_sum(float x) {
 // L mod 8): the decode, shared-prefix and split prefill kernels run KV head
 // g's workgroups there too (KV head fastest in their grids), so with H_kv a
 // multiple of 8 the merge reads the partials from the L2 they were written
-// through.
+// through.  Only while the partials fit the L2s: larger ones come from HBM
+// either way, and the plain row order reads them as one stream.
+constexpr int64_t kMergeFromL2Bytes = int64_t{16} << 20;  // half of the 8 XCDs' 4 MiB L2s
 __device__ __forceinline__ int64_t merge_row(int64_t L, int32_t H_q, int32_t H_kv) {
   const int G = H_q / H_kv;
   const int g = static_cast<int>(L % H_kv);

@@ -100,10 +100,10 @@ __global__ void __launch_bounds__(MAXT)
 template <typename E, int D>
 __global__ void __launch_bounds__(D)
     decode_merge_kernel(void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
-                        const int32_t* __restrict__ context_lens, int32_t H_q, int32_t H_kv, int32_t num_parts,
-                        int32_t part_tokens) {
+                        const int32_t* __restrict__ context_lens, int32_t H_q, int32_t H_kv, int32_t xcd_order,
+                        int32_t num_parts, int32_t part_tokens) {
   extern __shared__ float w_lds[];  // [num_parts] weights, then [1] total
-  const int64_t bh = merge_row(blockIdx.x, H_q, H_kv);
+  const int64_t bh = xcd_order ? merge_row(blockIdx.x, H_q, H_kv) : blockIdx.x;
   const int b = static_cast<int>(bh / H_q);
   const int e = threadIdx.x;
   const int ctx = context_lens[b];
@@ -208,9 +208,10 @@ void launch_decode_merge(int dtype, int D, void* out, const Workspace& ws, const
   const dim3 grid(static_cast<uint32_t>(B) * H_q);
   const size_t lds = pl.num_parts * sizeof(float);
   const int pt = pl.blocks_per_part * bs;
+  const int xcd = static_cast<int64_t>(B) * H_q * pl.num_parts * (D + 2) * 4 <= kMergeFromL2Bytes;
 #define PA_MERGE(E_, D_) \
   hipLaunchKernelGGL((decode_merge_kernel<E_, D_>), grid, dim3(D_), lds, stream, out, ws.ml, ws.acc, ctx, H_q, \
-                     H_kv, pl.num_parts, pt)
+                     H_kv, xcd, pl.num_parts, pt)
   if (dtype == PA_F32 && D == 64) PA_MERGE(F32, 64);
   if (dtype == PA_F32 && D == 128) PA_MERGE(F32, 128);
   if (dtype == PA_BF16 && D == 64) PA_MERGE(BF16, 64);

@@ -47,18 +47,19 @@ __global__ void __launch_bounds__(kPrefillThreads)
     prefill_chunk_kernel(const char* __restrict__ pool_k, const char* __restrict__ pool_v, int64_t layer_off,
                          int64_t head_stride, const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                          const int32_t* __restrict__ table, int32_t T, int32_t H_q, int32_t ctx_before,
-                         float scale_log2, int32_t num_splits, int32_t steps_per_split, float* __restrict__ ws_o,
-                         float* __restrict__ ws_ml) {
+                         float scale_log2, int32_t num_splits, int32_t steps_per_split, int32_t xcd_order,
+                         float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(1024))) PrefillLds<D> lds;
   // One (work item, key split) per workgroup; gridDim.x = ntiles * H_kv *
-  // num_splits.  Unsplit, consecutive ids take the items of one KV head, so
-  // its tiles, which read the same keys, share an XCD's L2.  Split, the KV
-  // head is fastest: head g's tiles and splits run on XCD g mod 8 (with H_kv
-  // a multiple of 8), where the merge takes head g's rows and finds their
+  // num_splits.  By default consecutive ids take the items of one split, so
+  // the tiles of one KV head, which read the same keys, share an XCD's L2.
+  // With xcd_order (a split whose partials fit the L2s) the KV head is
+  // fastest: head g's tiles and splits run on XCD g mod 8 (with H_kv a
+  // multiple of 8), where the merge takes head g's rows and finds their
   // partials in that XCD's L2.
   const int items = gridDim.x / num_splits;
   int w, split;
-  if (num_splits > 1) {
+  if (xcd_order) {
     constexpr int TP = kRowsPerWave * kPrefillWaves / G;
     const int ntiles = (T + TP - 1) / TP;
     const int H_kv = items / ntiles;
@@ -67,8 +68,9 @@ __global__ void __launch_bounds__(kPrefillThreads)
     w = (L % H_kv) * ntiles + rest % ntiles;
     split = rest / ntiles;
   } else {
-    w = xcd_contiguous(blockIdx.x, gridDim.x);
-    split = 0;
+    const int wl = xcd_contiguous(blockIdx.x, gridDim.x);
+    w = wl % items;
+    split = wl / items;
   }
   float* wo = nullptr;
   float* wml = nullptr;
@@ -90,9 +92,10 @@ template <typename E, int D>
 __global__ void __launch_bounds__(D)
     prefill_merge_kernel(void* __restrict__ out, const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                          int32_t T, int32_t H_q, int32_t G, int32_t ctx_before, int32_t num_splits,
-                         int32_t steps_per_split) {
+                         int32_t steps_per_split, int32_t xcd_order) {
   extern __shared__ float wt[];  // [num_splits] weights, then the total weight
-  const int64_t row = merge_row(blockIdx.x, H_q, H_q / G);  // pos * H_q + head, KV head g's rows on XCD g mod 8
+  // pos * H_q + head (with xcd_order: KV head g's rows on XCD g mod 8)
+  const int64_t row = xcd_order ? merge_row(blockIdx.x, H_q, H_q / G) : blockIdx.x;
   const int pos = static_cast<int>(row / H_q);
   const int e = threadIdx.x;
   const int TP = kRowsPerWave * kPrefillWaves / G;
@@ -209,14 +212,15 @@ static void launch_prefill(const pa_kv_pool* pool, int32_t layer, void* out, con
   const int64_t head_stride = static_cast<int64_t>(pool->num_blocks) * BS * D * 2;
   const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * head_stride;
   dim3 grid(static_cast<uint32_t>((T + TP - 1) / TP) * pool->num_kv_heads * pl.num_splits);
+  const int xcd = pl.num_splits > 1 && static_cast<int64_t>(prefill_ws_bytes(pl, T, H_q, D)) <= kMergeFromL2Bytes;
   hipLaunchKernelGGL((prefill_chunk_kernel<E, D, G, BS>), grid, dim3(kPrefillThreads), 0, stream,
                      static_cast<const char*>(pool->k), static_cast<const char*>(pool->v), layer_off, head_stride,
                      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out), table, T, H_q, ctx_before,
-                     scale_log2, pl.num_splits, pl.steps_per_split, ws_o, ws_ml);
+                     scale_log2, pl.num_splits, pl.steps_per_split, xcd, ws_o, ws_ml);
   if (pl.num_splits > 1)
     hipLaunchKernelGGL((prefill_merge_kernel<E, D>), dim3(static_cast<uint32_t>(T) * H_q), dim3(D),
                        (pl.num_splits + 1) * sizeof(float), stream, out, ws_o, ws_ml, T, H_q, G, ctx_before,
-                       pl.num_splits, pl.steps_per_split);
+                       pl.num_splits, pl.steps_per_split, xcd);
 }
 
 template <typename E, int D, int G>

@@ -524,11 +524,11 @@ template <typename E, int D>
 __global__ void __launch_bounds__(D)
     shared_merge_kernel(void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
                         const float* __restrict__ pre_o, const float* __restrict__ pre_ml,
-                        const int32_t* __restrict__ context_lens, int32_t H_q, int32_t H_kv, int32_t num_parts,
-                        int32_t blocks_per_part, int32_t bs, GroupList gl) {
+                        const int32_t* __restrict__ context_lens, int32_t H_q, int32_t H_kv, int32_t xcd_order,
+                        int32_t num_parts, int32_t blocks_per_part, int32_t bs, GroupList gl) {
   extern __shared__ float wt[];  // [max splits + num_parts] weights
   __shared__ float red[2];
-  const int64_t bh = merge_row(blockIdx.x, H_q, H_kv);
+  const int64_t bh = xcd_order ? merge_row(blockIdx.x, H_q, H_kv) : blockIdx.x;
   const int b = static_cast<int>(bh / H_q);
   const int hd = static_cast<int>(bh % H_q);
   const int e = threadIdx.x;
@@ -737,8 +737,9 @@ static void launch_shared(const pa_kv_pool* pool, int32_t layer, void* out, cons
   }
   const size_t lds = (p.max_splits + p.dec.num_parts) * sizeof(float);
   hipLaunchKernelGGL((shared_merge_kernel<E, D>), dim3(static_cast<uint32_t>(B) * H_q), dim3(D), lds, stream, out,
-                     ws_ml, ws_acc, pre_o, pre_ml, ctx, H_q, pool->num_kv_heads, p.dec.num_parts, p.dec.blocks_per_part,
-                     BS, p.gl);
+                     ws_ml, ws_acc, pre_o, pre_ml, ctx, H_q, pool->num_kv_heads,
+                     static_cast<int64_t>(shared_ws_bytes(p, B, H_q, D)) <= kMergeFromL2Bytes, p.dec.num_parts,
+                     p.dec.blocks_per_part, BS, p.gl);
 }
 
 template <typename E, int D, int G>
