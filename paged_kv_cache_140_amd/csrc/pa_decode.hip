@@ -48,9 +48,9 @@ __global__ void __launch_bounds__(MAXT)
     decode_kernel(char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off, int64_t head_stride,
                   const char* __restrict__ q, void* __restrict__ out, const int32_t* __restrict__ block_tables,
                   int32_t max_blocks, const int32_t* __restrict__ context_lens, float scale_log2, int32_t H_q,
-                  int32_t blocks_per_part, int32_t num_parts, int32_t waves, float* __restrict__ ws_ml,
-                  float* __restrict__ ws_acc, const char* __restrict__ k_new, const char* __restrict__ v_new,
-                  const int32_t* __restrict__ new_slots) {
+                  int32_t blocks_per_part, int32_t num_parts, int32_t unsplit_cus, int32_t waves,
+                  float* __restrict__ ws_ml, float* __restrict__ ws_acc, const char* __restrict__ k_new,
+                  const char* __restrict__ v_new, const int32_t* __restrict__ new_slots) {
   extern __shared__ float smem[];
   // Grid (kv head, partition slot, sequence), kv head fastest: workgroup i
   // runs on XCD i % 8, so with H_kv a multiple of 8 every XCD gets the same
@@ -62,6 +62,17 @@ __global__ void __launch_bounds__(MAXT)
   // of the sequence index spreads them.  (Measured on 63 contexts of
   // 1k-32k: 4 / 8 / 16 partitions 1,023 / 895 / 863 us unrotated, 788 /
   // 787 / 819 us rotated.)  Fewer than 4 partitions: no rotation, no cost.
+  if (decode_unsplit(context_lens, gridDim.z, BS, gridDim.x, unsplit_cus)) {
+    // Unsplit: the grid's first B * H_kv workgroups, in the order an unsplit
+    // grid would launch them, each decode one (sequence, KV head) whole and
+    // write its output; the others exit.
+    const int b = blockIdx.y + num_parts * blockIdx.z;
+    if (b >= static_cast<int>(gridDim.z)) return;
+    decode_body<E, D, G, BS, FUSED>(waves, blockIdx.x, 0, gridDim.x, b, smem, pool_k, pool_v, layer_off, head_stride,
+                                    q, out, block_tables, max_blocks, context_lens, scale_log2, H_q, max_blocks, 1,
+                                    ws_ml, ws_acc, k_new, v_new, new_slots);
+    return;
+  }
   int part = blockIdx.y;
   if (num_parts >= 4) {
     part += blockIdx.z & 3;
@@ -79,16 +90,34 @@ __global__ void __launch_bounds__(MAXT)
     gather_kernel(char* __restrict__ pool_k, char* __restrict__ pool_v, int64_t layer_off, int64_t head_stride,
                   const int32_t* __restrict__ block_tables, int32_t max_blocks,
                   const int32_t* __restrict__ context_lens, int32_t H_q, int32_t blocks_per_part, int32_t num_parts,
-                  int32_t waves, uint32_t* __restrict__ checksums) {
+                  int32_t unsplit_cus, int32_t waves, uint32_t* __restrict__ checksums) {
   extern __shared__ float smem[];
   int part = blockIdx.y;
-  if (num_parts >= 4) {
+  int b = blockIdx.z;
+  int bpp = blocks_per_part;
+  if (decode_unsplit(context_lens, gridDim.z, BS, gridDim.x, unsplit_cus)) {
+    // the decode's unsplit walk: the first B * H_kv workgroups take partition
+    // 0 of one (sequence, KV head) each, whole; the others stand for the
+    // empty partitions 1 .. P-1, whose checksums are 0
+    const int B = gridDim.z;
+    const int rest = blockIdx.y + num_parts * blockIdx.z;
+    if (rest >= B) {
+      const int e = rest - B;
+      if ((threadIdx.x & 63) == 0)
+        checksums[((static_cast<int64_t>(e / (num_parts - 1)) * num_parts + 1 + e % (num_parts - 1)) * gridDim.x +
+                   blockIdx.x) * waves + (threadIdx.x >> 6)] = 0;
+      return;
+    }
+    b = rest;
+    part = 0;
+    bpp = max_blocks;
+  } else if (num_parts >= 4) {
     part += blockIdx.z & 3;
     if (part >= num_parts) part -= num_parts;
   }
-  decode_body<E, D, G, BS, false, false, true>(waves, blockIdx.x, part, gridDim.x, blockIdx.z, smem, pool_k, pool_v,
+  decode_body<E, D, G, BS, false, false, true>(waves, blockIdx.x, part, gridDim.x, b, smem, pool_k, pool_v,
                                                layer_off, head_stride, nullptr, nullptr, block_tables, max_blocks,
-                                               context_lens, 0.0f, H_q, blocks_per_part, num_parts,
+                                               context_lens, 0.0f, H_q, bpp, num_parts,
                                                reinterpret_cast<float*>(checksums), nullptr, nullptr, nullptr,
                                                nullptr);
 }
@@ -101,11 +130,12 @@ template <typename E, int D>
 __global__ void __launch_bounds__(D)
     decode_merge_kernel(void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
                         const int32_t* __restrict__ context_lens, int32_t H_q, int32_t H_kv, int32_t xcd_order,
-                        int32_t num_parts, int32_t part_tokens) {
+                        int32_t num_parts, int32_t part_tokens, int32_t bs, int32_t unsplit_cus) {
   extern __shared__ float w_lds[];  // [num_parts] weights, then [1] total
   const int64_t bh = xcd_order ? merge_row(blockIdx.x, H_q, H_kv) : blockIdx.x;
   const int b = static_cast<int>(bh / H_q);
   const int e = threadIdx.x;
+  if (decode_unsplit(context_lens, gridDim.x / H_q, bs, H_kv, unsplit_cus)) return;  // the decode wrote out
   const int ctx = context_lens[b];
   const int np = min((ctx + part_tokens - 1) / part_tokens, num_parts);
   const float* ml = ws_ml + bh * num_parts * 2;
@@ -185,6 +215,10 @@ DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx) {
   // 797 us).
   p.waves = env_waves > 0 ? env_waves : 8;
   p.waves = p.waves > max_waves_for(G) ? max_waves_for(G) : p.waves;
+  // A split planned from max_ctx alone may run unsplit on the device
+  // (decode_unsplit), unless the partition length is fixed by a tuning
+  // override.
+  p.unsplit_cus = (p.num_parts > 1 && env_pb <= 0) ? cus : 0;
   return p;
 }
 
@@ -211,7 +245,7 @@ void launch_decode_merge(int dtype, int D, void* out, const Workspace& ws, const
   const int xcd = static_cast<int64_t>(B) * H_q * pl.num_parts * (D + 2) * 4 <= kMergeFromL2Bytes;
 #define PA_MERGE(E_, D_) \
   hipLaunchKernelGGL((decode_merge_kernel<E_, D_>), grid, dim3(D_), lds, stream, out, ws.ml, ws.acc, ctx, H_q, \
-                     H_kv, xcd, pl.num_parts, pt)
+                     H_kv, xcd, pl.num_parts, pt, bs, pl.unsplit_cus)
   if (dtype == PA_F32 && D == 64) PA_MERGE(F32, 64);
   if (dtype == PA_F32 && D == 128) PA_MERGE(F32, 128);
   if (dtype == PA_BF16 && D == 64) PA_MERGE(BF16, 64);
@@ -240,8 +274,8 @@ static void launch_decode(const pa_kv_pool* pool, int32_t layer, void* out, cons
   hipLaunchKernelGGL((decode_kernel<E, D, G, BS, max_threads<G>(), FUSED>), grid, dim3(64 * pl.waves), lds, stream,
                      static_cast<char*>(pool->k), static_cast<char*>(pool->v), layer_off, head_stride,
                      static_cast<const char*>(q), out, bt, max_blocks, ctx, scale_log2, H_q, pl.blocks_per_part,
-                     pl.num_parts, pl.waves, ws.ml, ws.acc, static_cast<const char*>(nt.k), static_cast<const char*>(nt.v),
-                     nt.slots);
+                     pl.num_parts, pl.unsplit_cus, pl.waves, ws.ml, ws.acc, static_cast<const char*>(nt.k),
+                     static_cast<const char*>(nt.v), nt.slots);
   if (pl.num_parts > 1) launch_decode_merge(pool->dtype, D, out, ws, ctx, B, H_q, pool->num_kv_heads, pl, BS, stream);
 }
 
@@ -386,7 +420,7 @@ static void launch_gather(const pa_kv_pool* pool, int32_t layer, int32_t B, cons
   dim3 grid(pool->num_kv_heads, pl.num_parts, B);
   hipLaunchKernelGGL((gather_kernel<E, D, G, BS, max_threads<G>()>), grid, dim3(64 * pl.waves), lds, stream,
                      static_cast<char*>(pool->k), static_cast<char*>(pool->v), layer_off, head_stride, bt, max_blocks,
-                     ctx, H_q, pl.blocks_per_part, pl.num_parts, pl.waves, cs);
+                     ctx, H_q, pl.blocks_per_part, pl.num_parts, pl.unsplit_cus, pl.waves, cs);
 }
 template <typename E, int D, int G>
 static GatherFn gather_bs(int bs) {

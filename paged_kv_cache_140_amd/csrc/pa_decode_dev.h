@@ -166,6 +166,35 @@ __device__ __forceinline__ void gather_heads(const uint32_t* own, uint32_t* all)
   }
 }
 
+// Whether a split decode runs unsplit, one partition per (sequence, KV
+// head): when the batch's longest sequence holds no more blocks than one
+// CU's share of the whole batch (the sum of all sequences' blocks times H_kv,
+// over the CU count), every (sequence, KV head) fits the share a CU would
+// stream anyway, and a split only adds partial writes and merge work.  The
+// host plans the grid from the longest context alone (the lengths stay on
+// the device), so it cannot tell a uniform mix of long contexts from one
+// long context among short ones; every workgroup of the decode and of its
+// merge reads the B lengths and takes the same decision.  Unsplit, the
+// first B * H_kv workgroups of the grid (in launch order) take one
+// (sequence, KV head) each and write its output as an unsplit decode does,
+// the rest exit, and the merge writes nothing.  cus <= 0: never.
+// Wave-uniform; every wave computes it on its own.
+__device__ __forceinline__ bool decode_unsplit(const int32_t* __restrict__ lens, int B, int BS, int H_kv, int cus) {
+  if (cus <= 0) return false;
+  int64_t sum = 0;
+  int longest = 0;
+  for (int i = threadIdx.x & 63; i < B; i += 64) {
+    const int n = (lens[i] + BS - 1) / BS;
+    sum += n;
+    longest = max(longest, n);
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    sum += __shfl_xor(sum, off);
+    longest = max(longest, __shfl_xor(longest, off));
+  }
+  return __builtin_amdgcn_readfirstlane(static_cast<int64_t>(longest) * cus <= sum * H_kv);
+}
+
 // One workgroup's share of a decode: KV head g of sequence b, partition
 // ``part`` (blocks [part, part + 1) * blocks_per_part), H_kv KV heads.  W is
 // the workgroup's wave count, passed in rather than read from the dispatch:

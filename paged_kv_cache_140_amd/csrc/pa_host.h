@@ -54,6 +54,9 @@ struct DecodePlan {
   int waves;
   int blocks_per_part;
   int num_parts;
+  // > 0: the device may run the split plan unsplit (decode_unsplit), given
+  // this CU count; 0: the partitions are as planned.
+  int unsplit_cus;
 };
 DecodePlan plan_decode(int B, int H_kv, int G, int bs, int max_ctx);
 

@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(kPrefillThreads)
                  // decode half
                  const char* __restrict__ dq, void* __restrict__ dout, const int32_t* __restrict__ block_tables,
                  int32_t max_blocks, const int32_t* __restrict__ context_lens, int32_t blocks_per_part,
-                 int32_t num_parts, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+                 int32_t num_parts, int32_t unsplit_cus, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
                  // prefill half
                  const uint16_t* __restrict__ pq, uint16_t* __restrict__ pout, const int32_t* __restrict__ ptables,
                  int32_t pt_stride, int32_t n_pre, ChunkList ch) {
@@ -92,6 +92,16 @@ __global__ void __launch_bounds__(kPrefillThreads)
   const int j = id - n_pre;
   const int g = j % H_kv;
   const int rest = j / H_kv;
+  // the decode kernel's unsplit decision and order, over the decode half's
+  // B rows
+  const int B = static_cast<int>((gridDim.x - n_pre) / (H_kv * num_parts));
+  if (decode_unsplit(context_lens, B, BS, H_kv, unsplit_cus)) {
+    if (rest >= B) return;
+    decode_body<E, D, G, BS, false>(kPrefillWaves, g, 0, H_kv, rest, reinterpret_cast<float*>(&lds[0][0]), pool_k,
+                                    pool_v, layer_off, head_stride, dq, dout, block_tables, max_blocks, context_lens,
+                                    scale_log2, H_q, max_blocks, 1, ws_ml, ws_acc, nullptr, nullptr, nullptr);
+    return;
+  }
   const int b = rest / num_parts;
   int part = rest % num_parts;
   if (num_parts >= 4) {
@@ -131,7 +141,7 @@ static void launch_mixed(const pa_kv_pool* pool, const MixedLaunch& m, hipStream
   hipLaunchKernelGGL((mixed_kernel<E, D, G, BS>), grid, dim3(kPrefillThreads), 0, stream, static_cast<char*>(pool->k),
                      static_cast<char*>(pool->v), m.layer_off, m.head_stride, pool->num_kv_heads, m.H_q, m.scale_log2,
                      static_cast<const char*>(m.dq), m.dout, m.bt, m.max_blocks, m.ctx, m.pl.blocks_per_part,
-                     m.pl.num_parts, m.ws.ml, m.ws.acc, static_cast<const uint16_t*>(m.pq),
+                     m.pl.num_parts, m.pl.unsplit_cus, m.ws.ml, m.ws.acc, static_cast<const uint16_t*>(m.pq),
                      static_cast<uint16_t*>(m.pout), m.ptables, m.pt_stride, m.n_pre, m.ch);
 }
 

@@ -322,6 +322,59 @@ def test_decode_large_batch_and_long_context():
     assert max_abs_err(out, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("balanced", [True, False])
+def test_decode_split_plan_runs_unsplit_only_when_balanced(balanced):
+    """A split planned from max_ctx alone runs unsplit on the device when the
+    longest sequence holds no more blocks than one CU's share of the batch
+    (all B lengths are read by every workgroup).  Both batches below get the
+    same 4-partition grid; the balanced one (40 contexts of 4,100-4,200
+    tokens) writes its outputs directly and leaves the split workspace
+    untouched, the other (one 4,200-token context among 39 of 100) writes
+    every row's first partition and all four of its long sequence's.  Both
+    match the oracle."""
+    from paged_kv_cache_140_amd import decode_workspace, pa_decode
+    from paged_kv_cache_140_amd.runner import to_device
+
+    H_q, H_kv, d, bs, dtype = 16, 8, 128, 16, "bf16"
+    rng = np.random.default_rng(41 if balanced else 42)
+    B = 40
+    if balanced:
+        lengths = [int(x) for x in rng.integers(4100, 4201, size=B)]
+    else:
+        lengths = [100] * B
+        lengths[17] = 4200
+    say("decode unsplit decision", "balanced" if balanced else "one long")
+    op, gp, tables = _world(rng, lengths, H_q, H_kv, d, bs, dtype, poison=False)
+    maxb = max(len(t) for t in tables)
+    tab = np.zeros((B, maxb), dtype=np.int32)
+    for i, t in enumerate(tables):
+        tab[i, :len(t)] = t
+    max_ctx = 4200
+    q32 = rng.standard_normal((B, H_q, d)).astype(np.float32)
+    q = to_device(q32, dtype, "cuda")
+    out = torch.full_like(q, float("nan"))
+    ws = decode_workspace(gp, B, H_q, max_ctx)
+    assert ws is not None, "the plan must split"
+    P = ws.numel() // (B * H_q * (d + 2) * 4)
+    assert P == 4
+    ws.fill_(0xFF)  # NaN bit patterns
+    pa_decode(gp, 0, out, q, torch.from_numpy(tab).cuda(), torch.tensor(lengths, dtype=torch.int32).cuda(), max_ctx,
+              0.088, ws)
+    torch.cuda.synchronize()
+    ref = attention.decode(op, 0, widen(q32, dtype), tables, lengths, 0.088)
+    assert max_abs_err(f64(out), ref) <= TOL[dtype]
+    ml = ws[:B * H_q * P * 2 * 4].view(torch.float32).view(B, H_q, P, 2).cpu().numpy()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nblk = [-(-n // bs) for n in lengths]
+    unsplit = max(nblk) * cus <= sum(nblk) * H_kv
+    assert unsplit == balanced
+    if unsplit:
+        assert np.all(np.isnan(ml))
+    else:
+        assert np.all(np.isfinite(ml[:, :, 0]))
+        assert np.all(np.isfinite(ml[17, :, 1:]))  # the long sequence's partitions 1-3
+
+
 @pytest.mark.parametrize("plan", [(8, 4), (4, 1), (16, 3)])
 def test_decode_graph_replay_matches_eager(plan, tune):
     """Split decodes captured in one graph (several launches sharing one
