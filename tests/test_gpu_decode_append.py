@@ -160,6 +160,34 @@ def test_fused_edge_shapes_and_splits(case, plan, tune):
     assert err <= TOL[dtype]
 
 
+def test_fused_balanced_split_plan_runs_unsplit():
+    """40 contexts of 4,100-4,200 tokens (GQA 16/8): the plan splits (from
+    max_ctx alone) and the device runs the batch unsplit, each workgroup
+    writing its new token and its output itself.  Pool bits and outputs
+    match the oracle; the new rows start as NaN in the pool."""
+    H_q, H_kv, d, bs, dtype = 16, 8, 128, 16, "bf16"
+    rng = np.random.default_rng(43)
+    lengths = [int(x) for x in rng.integers(4100, 4201, size=40)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nblk = [-(-n // bs) for n in lengths]
+    assert max(nblk) * cus <= sum(nblk) * H_kv  # the batch is balanced
+    say("decode_append unsplit on the device")
+    bm, op, N, slots = _history(rng, lengths, H_kv, d, bs, dtype)
+    gp = _gpu_pool(op, H_kv, N, bs, d, dtype)
+    B = len(lengths)
+    kn = rng.standard_normal((B, H_kv, d)).astype(np.float32)
+    vn = rng.standard_normal((B, H_kv, d)).astype(np.float32)
+    q32 = rng.standard_normal((B, H_q, d)).astype(np.float32)
+    tables = [bm.block_table(i) for i in range(B)]
+    out = _fused(gp, q32, kn, vn, slots, tables, lengths, 0.088, dtype)
+    op.append(0, encoding.encode(kn, dtype), encoding.encode(vn, dtype), slots)
+    ref = attention.decode(op, 0, widen(q32, dtype), tables, lengths, 0.088)
+    assert np.array_equal(bits(gp.k), op.k) and np.array_equal(bits(gp.v), op.v)
+    err = max_abs_err(f64(out), ref)
+    say("  max abs err", err)
+    assert err <= TOL[dtype]
+
+
 def test_fused_negative_slot_reads_the_pool():
     """A negative slot skips that sequence's write; its newest position is
     then read from the pool (here already holding the token), not from the

@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
     (64, 8, 128, 16, [4096, 1024, 32768], None),
     (16, 8, 128, 32, [640, 64, 96], 3),
     (32, 8, 64, 8, [160, 48, 992], 5),
+    # a split plan that the device runs unsplit (40 balanced long contexts):
+    # the empty partition slots' checksums are written as 0
+    (16, 8, 128, 16, [4096 + 16 * (i % 5) for i in range(40)], None),
 ])
 @pytest.mark.parametrize("waves", [4, 8])
 def test_gather_checksum_reads_every_visible_token_once(H_q, H_kv, d, bs, lengths, part_blocks, waves, tune):
