@@ -190,8 +190,12 @@ static double chunk_steps(const pa_kv_pool* pool, const ChunkList& ch, int G) {
 
 // Prefill workgroups when the caller leaves the choice to the library: enough
 // that the chunks end a little before the decode half would on its own (the
-// margin, 1.5x, is where sweeps of the 63-sequence decode with one 1,024-row
-// chunk and with four 256-row chunks bottom out; the curve is flat around it).
+// margin, 1.25x, is where sweeps of the 63-sequence decode with one 1,024-row
+// chunk and with four 256-row chunks bottom out, at n = 56 and n = 40: one
+// box, two alternations, 782-785 and 766-774 us against 809-822 and 787-789
+// us at n = 64).  Since the decode runs such batches unsplit, its workgroups
+// are long (a 32k context is one workgroup per KV head), and leaving it more
+// CUs pays more than the chunks finishing early.
 // Estimates: a 64-key step of one 256-row item takes ~2 us at head_dim 128
 // (less at 64); the decode streams half of B * max_ctx tokens per KV head at
 // ~5 TB/s.  Rounded up to a multiple of 8 (whole rounds per XCD), at most
@@ -204,7 +208,7 @@ static int default_prefill_wgs(const pa_kv_pool* pool, int B, int max_ctx, const
                            5.0e6;
   const int cap = std::min(n_items, device_cus());
   if (decode_us <= 0.0) return cap;
-  int n = static_cast<int>(std::ceil(1.5 * prefill_cu_us / decode_us));
+  int n = static_cast<int>(std::ceil(1.25 * prefill_cu_us / decode_us));
   n = static_cast<int>(ceil_div(std::max(n, 8), 8) * 8);
   return std::min(n, cap);
 }
