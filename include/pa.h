@@ -99,7 +99,11 @@ int pa_copy_blocks(const pa_kv_pool* pool, const int32_t* pairs, int32_t n, hipS
 /*
  * Workspace bytes ``pa_decode`` needs for a batch (0 when it will not split a
  * sequence over several workgroups).  Depends on host-side sizes, the
- * current device's CU count and the tuning overrides only.
+ * current device's CU count and the tuning overrides only.  A split planned
+ * from max_ctx may still run unsplit: the kernels read context_lens and,
+ * when the longest sequence holds no more blocks than one CU's share of the
+ * batch, decode each (sequence, KV head) whole and leave the workspace
+ * untouched (not with a PA_TUNE_DECODE_PART_BLOCKS override).
  */
 size_t pa_decode_workspace_size(const pa_kv_pool* pool, int32_t B, int32_t H_q, int32_t max_ctx);
 
@@ -357,7 +361,8 @@ int pa_set_validate(int on);
  *   PA_TUNE_DECODE_WAVES:       waves per decode workgroup (capped at 16, or
  *                               8 with more than 2 query heads per KV head).
  *   PA_TUNE_DECODE_PART_BLOCKS: blocks per decode partition (a sequence
- *                               longer than that is split and merged).
+ *                               longer than that is split and merged,
+ *                               however the lengths fall).
  *   PA_TUNE_PREFILL_SPLITS:     1 never splits a prefill chunk over its keys;
  *                               n > 1 asks for n splits whenever the caller
  *                               gives a workspace.
