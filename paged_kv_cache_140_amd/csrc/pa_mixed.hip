@@ -191,9 +191,10 @@ static double chunk_steps(const pa_kv_pool* pool, const ChunkList& ch, int G) {
 // Prefill workgroups when the caller leaves the choice to the library: enough
 // that the chunks end a little before the decode half would on its own (the
 // margin, 1.25x, is where sweeps of the 63-sequence decode with one 1,024-row
-// chunk and with four 256-row chunks bottom out, at n = 56 and n = 40: one
-// box, two alternations, 782-785 and 766-774 us against 809-822 and 787-789
-// us at n = 64).  Since the decode runs such batches unsplit, its workgroups
+// chunk and with four 256-row chunks bottom out: one box, two alternations,
+// 782-785 us at n = 56 for the one chunk, 766-776 us at n = 40-48 for the
+// four, against 809-822 and 787-789 us at n = 64; the margin gives 56 and
+// 48).  Since the decode runs such batches unsplit, its workgroups
 // are long (a 32k context is one workgroup per KV head), and leaving it more
 // CUs pays more than the chunks finishing early.
 // Estimates: a 64-key step of one 256-row item takes ~2 us at head_dim 128
