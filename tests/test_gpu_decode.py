@@ -375,6 +375,42 @@ def test_decode_split_plan_runs_unsplit_only_when_balanced(balanced):
         assert np.all(np.isfinite(ml[17, :, 1:]))  # the long sequence's partitions 1-3
 
 
+def test_decode_unsplit_counts_every_block_once():
+    """A balanced batch that runs unsplit (40 contexts of 4,100-4,200
+    tokens, GQA 16/8, bf16), with scale 0 (every visible token weighs the
+    same) and V rows that mark their logical block: every token of block j
+    holds 32 in dimension j mod 128 and 0 elsewhere.  The output is then the
+    share of the sequence's tokens in each block class, times 32: a block
+    dropped or read twice moves one dimension by 16 * 32 / ctx >= 0.12, six
+    times the bf16 bar (checked below on the oracle's side), so the test
+    fails on any block the walk misses or repeats."""
+    H_q, H_kv, d, bs, dtype = 16, 8, 128, 16, "bf16"
+    rng = np.random.default_rng(45)
+    B = 40
+    lengths = [int(x) for x in rng.integers(4100, 4201, size=B)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nblk = [-(-n // bs) for n in lengths]
+    assert max(nblk) * cus <= sum(nblk) * H_kv  # runs unsplit
+    op, gp, tables = _world(rng, lengths, H_q, H_kv, d, bs, dtype, poison=False)
+    amp = 32.0
+    marks = np.zeros(op.v.shape, dtype=np.float32)  # [L][H_kv][N][bs][d]
+    for t in tables:
+        for j, phys in enumerate(t):
+            marks[0, :, phys, :, j % d] = amp
+    op.v[...] = encoding.encode(marks, dtype)
+    gp.v.view(torch.int16).copy_(torch.from_numpy(op.v.view(np.int16)))
+    q32 = rng.standard_normal((B, H_q, d)).astype(np.float32)
+    say("decode unsplit block marks")
+    out = f64(_gpu_decode(gp, q32, tables, lengths, 0.0, dtype))
+    ref = attention.decode(op, 0, widen(q32, dtype), tables, lengths, 0.0)
+    # the oracle side: every sequence without its (full) logical block 1
+    # differs from the reference by more than five times the bar
+    short = attention.decode(op, 0, widen(q32, dtype), [t[:1] + t[2:] for t in tables],
+                             [n - bs for n in lengths], 0.0)
+    assert np.min(np.max(np.abs(short - ref), axis=(1, 2))) > 5 * TOL[dtype]
+    assert max_abs_err(out, ref) <= TOL[dtype]
+
+
 def test_decode_unsplit_fp32_mha_with_an_empty_sequence():
     """The unsplit path at fp32, one query head per KV head, d = 64, with an
     empty sequence in the batch (its rows are zeros) and a graph replayed
