@@ -26,7 +26,10 @@
 //    wave are merged by cross-lane shuffles, the waves of a workgroup through
 //    LDS.
 //  * a sequence split over several partitions writes (m, l, acc) partials
-//    to the workspace and a small merge kernel combines them.
+//    to the workspace and a small merge kernel combines them.  The grid is
+//    planned from max_ctx; the workgroups read all lengths and, when no
+//    sequence is longer than a CU's share of the batch, run unsplit
+//    instead (decode_unsplit) and the merge writes nothing.
 //  * fused append (pa_decode_append, FUSED): the step's new token of each
 //    sequence, at position ctx - 1, is written into its slot by the
 //    workgroup whose partition holds that position; that workgroup's paged
