@@ -186,9 +186,11 @@ int pa_decode_noalloc(const pa_kv_pool* pool, int32_t layer, void* out, const vo
  *   checksums: device uint32, at least pa_gather_checksum_size(...) bytes;
  *        entry ((b * P + p) * H_kv + g) * W + w is wave w of partition p
  *        of (sequence b, KV head g) (P partitions, W waves: pa_decode's
- *        plan).  The XOR of a (b, g)'s entries is the XOR of the K and V
- *        dwords of every token of the units its waves read (every visible
- *        token; at a partly filled last unit, its whole unit).
+ *        plan; when pa_decode would run the plan unsplit, so does this walk,
+ *        and the entries of partitions 1 .. P-1 are 0).  The XOR of a
+ *        (b, g)'s entries is the XOR of the K and V dwords of every token
+ *        of the units its waves read (every visible token; at a partly
+ *        filled last unit, its whole unit).
  *   Everything else as pa_decode (no q, no out, no workspace).
  */
 size_t pa_gather_checksum_size(const pa_kv_pool* pool, int32_t B, int32_t H_q, int32_t max_ctx);
